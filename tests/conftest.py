@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size workload, several seconds or more")
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """The HIP library on cuda:0; fails loudly if either is missing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    from quantized_kv_cache_kvq_amd import lib
+    lib.load()
+    return torch.device("cuda:0")

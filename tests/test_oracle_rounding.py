@@ -1,0 +1,53 @@
+"""Pins of oracle.rounding against exact rational rounding."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle.rounding import f16_bits, f16_from_bits, rn16, rn32, rne
+from tests.exact import rn16_exact, rn32_exact, rne_int
+
+
+def _samples(rng, n):
+    # mix of magnitudes, fp16 midpoints +- tiny offsets, subnormal range
+    a = rng.standard_normal(n) * np.exp(rng.uniform(-20, 12, n))
+    h = rng.standard_normal(n).astype(np.float16).astype(np.float64)
+    ulp = np.spacing(np.abs(h).astype(np.float16)).astype(np.float64)
+    mids = h + ulp / 2
+    near = mids + rng.choice([-1, 1], n) * np.abs(mids) * 2.0 ** -45
+    return np.concatenate([a, mids, near, [0.0, -0.0, 65504.0, 65519.99, 6.0e-8, 3.0e-8]])
+
+
+@pytest.mark.filterwarnings("ignore:overflow")
+def test_rn16_matches_exact_rational():
+    rng = np.random.default_rng(1)
+    xs = _samples(rng, 400)
+    got = rn16(xs)
+    for x, g in zip(xs, got):
+        want = rn16_exact(Fraction(float(x)))
+        if isinstance(want, float):
+            assert np.isinf(g) and np.sign(g) == np.sign(want)
+        else:
+            assert Fraction(float(g)) == want, (x, g, want)
+
+
+def test_rn32_matches_exact_rational():
+    rng = np.random.default_rng(2)
+    xs = rng.standard_normal(400) * np.exp(rng.uniform(-30, 30, 400))
+    got = rn32(xs)
+    for x, g in zip(xs, got):
+        assert Fraction(float(g)) == rn32_exact(Fraction(float(x)))
+
+
+def test_rne_ties_to_even():
+    vals = np.array([-2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5, 2.4999, 2.5001])
+    assert list(rne(vals)) == [-2, -2, -0, 0, 2, 2, 4, 2, 3]
+    for v in vals:
+        assert rne(v) == rne_int(Fraction(float(v)))
+
+
+def test_f16_bits_roundtrip():
+    x = np.array([0.0, 1.0, -2.0, 65504.0, 6.1035e-05], dtype=np.float16)
+    assert list(f16_bits(x)) == [0x0000, 0x3C00, 0xC000, 0x7BFF, 0x0400]
+    assert np.array_equal(f16_from_bits(f16_bits(x)), x)
