@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the packed KV cache on one MI355X.
+
+A step is one pass of the hot path over one synthetic batch: append the new
+token's K and V to every layer (quantise, pack, tail copy), decode attention
+of every query head over the whole cache, and, for the mixed-codec workload,
+one layer transcode.  Inputs are resident in HBM before timing starts.  To
+keep the step honest about HBM (the 256 MB Infinity Cache would otherwise
+hold a 57 MB cache), consecutive steps rotate over replicas of the cache
+whose total size exceeds the Infinity Cache.
+
+Prints one JSON line (rank 0, one GPU):
+  value = algorithmic packed-KV bytes read per step / step time  (GB/s)
+  roofline = the decode kernels' achieved bytes/s against 8 TB/s
+  cpu_baseline = the fp64 oracle decoding a bounded sample on the host.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+from quantized_kv_cache_kvq_amd import calib, lib  # noqa: E402
+from quantized_kv_cache_kvq_amd.cache import LayerCache, PlaneSpec  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+DEFAULT = "gqa4_q8k_q4v_tail1024"
+BITS = {c: (16 if c == "f16" else int(c[1])) for c in lib.CODECS}
+
+
+def row_total_bytes(codec, n=128):
+    """Codes + scales (+ mins) of one token of one head."""
+    if codec == "f16":
+        return 2 * n
+    L = min(32, n)
+    side = (2 if codec.endswith("_0") else 4) * (n // L)
+    return n * BITS[codec] // 8 + side
+
+
+def layer_bytes(wl, kc, vc, T):
+    """Algorithmic bytes one decode of a layer reads at T cached tokens."""
+    N = min(wl.N, T)
+    body = T - N
+    per_head = 0
+    if wl.basis == "lowrank":
+        for r, b in wl.lowrank[: wl.Hkv]:
+            per_head += 2 * row_total_bytes("q%d_1" % b, r)
+        per_tok = per_head
+    else:
+        per_tok = wl.Hkv * (row_total_bytes(kc) + row_total_bytes(vc))
+    return wl.B * (body * per_tok + N * wl.Hkv * 2 * 256)
+
+
+def plane_specs(wl, layer, codec=None):
+    if wl.basis == "plain":
+        c = codec or wl.kcodec
+        return PlaneSpec(c), PlaneSpec(codec or wl.vcodec)
+    if wl.basis == "hadamard":
+        return (PlaneSpec(wl.kcodec, "hadamard", w=synth.kvarn_normalizers(wl, layer, "k")),
+                PlaneSpec(wl.vcodec, "hadamard", w=synth.kvarn_normalizers(wl, layer, "v")))
+    ranks = [r for r, _ in wl.lowrank[: wl.Hkv]]
+    hc = ["q%d_1" % b for _, b in wl.lowrank[: wl.Hkv]]
+    P = calib.lowrank_projections([synth.basis(wl, layer, h).numpy() for h in range(wl.Hkv)], ranks)
+    s = PlaneSpec("", "lowrank", proj=P, ranks=ranks, head_codecs=hc)
+    return s, s
+
+
+def build_layer(wl, layer, codec, dev, capacity):
+    ks, vs = plane_specs(wl, layer, codec)
+    cache = LayerCache(wl.B, wl.Hkv, capacity, wl.N, ks, vs, dev)
+    k = synth.layer_rows(wl, layer, "k", device=dev)
+    v = synth.layer_rows(wl, layer, "v", device=dev)
+    cache.append(k[:, : wl.T - 1], v[:, : wl.T - 1])
+    new = (k[:, wl.T - 1:].contiguous(), v[:, wl.T - 1:].contiguous())
+    del k, v
+    return cache, new
+
+
+def clone_layer(src):
+    dst = LayerCache(src.batch, src.n_kv_heads, src.capacity, src.tail_len, src.kspec,
+                     src.vspec, src.device)
+    for name in ("k", "v"):
+        for key, t in src.bufs[name].items():
+            if t is not None:
+                dst.bufs[name][key].copy_(t)
+    dst.n_tokens = src.n_tokens
+    return dst
+
+
+def setup(wl, dev, replicas):
+    """Layer caches (per replica, per layer), new-token inputs and queries."""
+    capacity = math.ceil(wl.T / 64) * 64
+    codecs = synth.vbr_schedule(wl) if wl.layers > 1 else (None,)
+    base, news = [], []
+    for layer, codec in enumerate(codecs):
+        c, new = build_layer(wl, layer, codec, dev, capacity)
+        base.append(c)
+        news.append(new)
+    reps = [base] + [[clone_layer(c) for c in base] for _ in range(replicas - 1)]
+    qs = [synth.queries(wl, layer, device=dev) for layer in range(len(codecs))]
+    return reps, news, qs, codecs
+
+
+def cpu_baseline(wl, reps_layers, budget_s=20.0):
+    """The oracle (as it stands) decoding a bounded sample of the step on the
+    host: whole (batch entry, kv head) units of layer 0, as many as fit the
+    budget, on a thread pool of the host's cores (BLAS pinned to one thread
+    per worker).  Scaled to the full step's bytes."""
+    import concurrent.futures
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.layer as OL
+    from oracle import attention
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    layer = reps_layers[0]
+    k = synth.layer_rows(wl, 0, "k").numpy() if wl.T <= 40000 else None
+    if k is None:
+        return None
+    v = synth.layer_rows(wl, 0, "v").numpy()
+    q = synth.queries(wl, 0).numpy()
+    kspec = OL.PlaneSpec(wl.kcodec)
+    vspec = OL.PlaneSpec(wl.vcodec)
+    G = wl.Hq // wl.Hkv
+    N, T = wl.N, wl.T
+    units = [(b, h) for b in range(wl.B) for h in range(wl.Hkv)]
+    prepared = {}
+    for (b, h) in units:
+        xk, xv = k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1]
+        prepared[(b, h)] = (OL.encode_plane(xk, kspec), OL.encode_plane(xv, vspec),
+                            OL.tail_ring(xk, N), OL.tail_ring(xv, N))
+
+    def unit(bh):
+        b, h = bh
+        ke, ve, kt, vt = prepared[bh]
+        with threadpool_limits(1):
+            Kt = OL.attention_kv(ke, kt, kspec, T, N)
+            Vt = OL.attention_kv(ve, vt, vspec, T, N)
+            return attention.attend(q[b, h * G:(h + 1) * G], Kt[0], Vt[0], wl.sm_scale)
+
+    t0 = time.perf_counter()
+    done = 0
+    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+        while done < len(units) and time.perf_counter() - t0 < budget_s:
+            batch = units[done: done + cores]
+            list(ex.map(unit, batch))
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    frac = done / len(units)
+    step_s = dt / frac
+    nbytes = layer_bytes(wl, wl.kcodec, wl.vcodec, T)
+    return {"value": nbytes / step_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d (batch entry, kv head) units of the step's decode (fp64 dequant + "
+                      "softmax attention over %d tokens), %.2f s wall, scaled to the full step"
+                      % (done, len(units), T, dt),
+            "seconds_per_step": step_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT, choices=synth.ORDER)
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    lib.load()
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    if wl.name == "tiny":
+        wl = wl.with_(T=256)
+    codecs = synth.vbr_schedule(wl) if wl.layers > 1 else (wl.kcodec,)
+    step_bytes = sum(layer_bytes(wl, c if wl.layers > 1 else wl.kcodec,
+                                 c if wl.layers > 1 else wl.vcodec, wl.T) for c in codecs)
+    replicas = args.replicas or max(1, math.ceil(2 * MALL_BYTES / max(step_bytes, 1)))
+    replicas = min(replicas, 16)
+    print("setting up %s: %d layer(s), %d replica(s), %.1f MB read per step"
+          % (wl.name, len(codecs), replicas, step_bytes / 1e6), file=sys.stderr, flush=True)
+    reps, news, qs, _ = setup(wl, dev, replicas)
+    outs = [torch.empty_like(q) for q in qs]
+    transcode_dst = None
+    if wl.layers > 1:
+        src = [i for i, c in enumerate(codecs) if c == "f16"][0]
+        s = reps[0][src]
+        transcode_dst = (src, LayerCache(s.batch, s.n_kv_heads, s.capacity, s.tail_len,
+                                         PlaneSpec("q8_0"), PlaneSpec("q8_0"), dev,
+                                         share_tail_with=s))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        layers = reps[i % len(reps)]
+        for li, c in enumerate(layers):
+            c.n_tokens = wl.T - 1
+            c.append(news[li][0], news[li][1])
+            if ev is not None:
+                ev[0].record(stream)
+            c.decode(qs[li], wl.sm_scale, out=outs[li])
+            if ev is not None:
+                ev[1].record(stream)
+        if transcode_dst is not None:
+            src, dst = transcode_dst
+            layers[src].transcode_into(dst)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # decode launches, bracketed one by one on the launch stream
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, pairs[i] if len(codecs) == 1 else None)
+    torch.cuda.synchronize()
+    if len(codecs) == 1:
+        dec_ms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
+        dec_bytes = step_bytes
+    else:
+        dec_ms, dec_bytes = None, None
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ctx_tok_s = wl.B * wl.T * len(codecs) / (ms_per_step * 1e-3)
+    roof = None
+    if dec_ms:
+        ach = dec_bytes / (dec_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode attention (split kernel + combine)", "avg_launch_us": round(dec_ms * 1e3, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, reps[0])
+        if cpu is not None:
+            cpu.pop("seconds_per_step", None)
+    line = {
+        "metric": "decode-attention packed-KV GB/s and % of 8 TB/s HBM peak; context tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded), resident in HBM; %d cache replicas rotated per step" % replicas,
+        "config": {"workload": wl.name, "batch": wl.B, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
+                   "context": wl.T, "tail": wl.N, "k_codec": wl.kcodec or "per-head",
+                   "v_codec": wl.vcodec or "per-head", "basis": wl.basis, "layers": len(codecs),
+                   "bytes_per_step": step_bytes},
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "context_tokens_per_s": round(ctx_tok_s, 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

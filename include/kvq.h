@@ -1,0 +1,186 @@
+/*
+ * kvq.h - packed low-bit KV cache and single-query decode attention on
+ * AMD Instinct MI355X (gfx950).  C ABI of libkvq.so.
+ *
+ * What the library computes (sources are the pages this format follows):
+ *
+ *  - Block codecs.  The BeeLlama.cpp v0.4.0 release notes (new standard KV
+ *    cache types) name the family: q8/q6/q5/q4/q3/q2 in an absmax "_0" and a
+ *    min-offset "_1" flavour.  A block is 32 consecutive channels of one
+ *    token of one (batch, kv head) with one binary16 scale (plus one binary16
+ *    min for _1):
+ *      _0: d = RN16(amax/qmax), qmax = 2^(b-1)-1, q = clamp(rne(x/d), +-qmax)
+ *      _1: m = RN16(min x), y = RN32(x-m), d = RN16(RN32(max x - m)/(2^b-1)),
+ *          u = clamp(rne(y/d), 0, 2^b-1); value RN32(u*d + m)
+ *    (all quotients exact, ties to even; d == 0 gives zero codes).
+ *  - Precision tail (same release notes, precision-tail section): the newest
+ *    tail_len tokens are also kept as binary16 in a ring (token t in slot
+ *    t mod tail_len) and decode reads them from there; codes are written for
+ *    every token at append time.
+ *  - KVarN basis (same release notes, KVarN section; KV-COBRA explainer,
+ *    jargon on the Hadamard rotation): stored coordinates are
+ *    y = H (x * w) with w = 1/sigma per channel (caller-supplied) and H the
+ *    unnormalised order-128 Sylvester Hadamard matrix.
+ *  - Low-rank basis (KV-COBRA explainer: per-head rank and bits, rotation
+ *    fused into the projection): stored coordinates are u = P_h^T x with a
+ *    caller-supplied binary16 P_h (128 x rank_h), coded with a per-head codec
+ *    on blocks of min(32, rank_h); attention runs in rank space.
+ *  - Per-layer codecs and transcoding (VBR announcement thread, opening
+ *    posts): each layer and each of K/V carries its own codec; a layer can be
+ *    re-encoded to another codec as the session grows.
+ *  - Decode attention (forum thread on decode bandwidth, second post): the
+ *    newest query is dotted with every cached key, softmax over the scores,
+ *    weighted sum of the cached values.  Query head h reads kv head
+ *    h / (n_q_heads / n_kv_heads).
+ *
+ * Conventions for every entry point:
+ *  - Every pointer in a descriptor is device memory owned by the caller,
+ *    except kvq_plane.rank and kvq_plane.head_codec (host arrays).
+ *  - The library never allocates, frees or synchronises; work is enqueued on
+ *    `stream` (a hipStream_t, NULL = the default stream) and runs
+ *    asynchronously.  Descriptors are read, never modified.
+ *  - All checks run on the host before anything is enqueued: on any error
+ *    nothing is launched and the status says why (detail in kvq_last_error).
+ *    A failed launch returns KVQ_ERR_HIP.
+ *  - Values that are NaN/Inf or large enough to overflow a binary16 scale
+ *    (|x| > 65504*qmax) are outside the contract and not detected.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_HEAD_DIM 128        /* the only supported head_dim */
+#define KVQ_TILE_TOKENS 64      /* capacity and tail_len are multiples of this */
+#define KVQ_MAX_LOWRANK_HEADS 32
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = 1,    /* null pointer, bad shape, bad enum value */
+    KVQ_ERR_UNSUPPORTED = 2,    /* valid but unsupported combination */
+    KVQ_ERR_CAPACITY = 3,       /* n_tokens + n_new > capacity */
+    KVQ_ERR_WORKSPACE = 4,      /* workspace missing or too small */
+    KVQ_ERR_HIP = 5             /* a HIP launch failed */
+} kvq_status;
+
+typedef enum kvq_codec {
+    KVQ_F16 = 0,
+    KVQ_Q8_0 = 1, KVQ_Q6_0 = 2, KVQ_Q5_0 = 3, KVQ_Q4_0 = 4, KVQ_Q3_0 = 5, KVQ_Q2_0 = 6,
+    KVQ_Q8_1 = 7, KVQ_Q6_1 = 8, KVQ_Q5_1 = 9, KVQ_Q4_1 = 10, KVQ_Q3_1 = 11, KVQ_Q2_1 = 12,
+    KVQ_Q1_1 = 13,
+    KVQ_NUM_CODECS = 14
+} kvq_codec;
+
+typedef enum kvq_basis {
+    KVQ_BASIS_PLAIN = 0,        /* channels as given */
+    KVQ_BASIS_HADAMARD = 1,     /* y = H (x * w)      (KVarN) */
+    KVQ_BASIS_LOWRANK = 2       /* u = P_h^T x        (KV-COBRA style) */
+} kvq_basis;
+
+/*
+ * One of K or V of one layer.
+ *
+ * Device layout (capacity C, B batch entries, Hkv kv heads; one "plane" per
+ * (batch entry, kv head) in that order):
+ *  - codes: each plane holds C rows; a row is one token's n stored
+ *    coordinates (n = 128, or rank_h for LOWRANK) as a little-endian
+ *    bitstream, coordinate e at bits [e*b, e*b+b) (_0 codes two's
+ *    complement, _1 unsigned), or n binary16 values for KVQ_F16.  Rows are
+ *    tiled by 64 tokens: with R the row size in bytes and c the largest of
+ *    16, 8, 4, 2, 1 dividing R, chunk k (c bytes) of token t is at byte
+ *    (t/64)*64*R + (k*64 + t%64)*c of the plane.  Planes are back to back
+ *    (LOWRANK planes have per-head sizes, in (batch, head) order).
+ *  - scales / mins: binary16 bit patterns, per plane [C][n/L] token-major
+ *    (L = 32, or min(32, rank_h)); mins only for _1 codecs (NULL otherwise);
+ *    both NULL for KVQ_F16.
+ *  - tail: binary16 rows of the raw (unrotated, unprojected) vectors,
+ *    [B][Hkv] planes of tail_len rows in the same 64-token tiled layout
+ *    (R = 256).  NULL when tail_len == 0.
+ * Sizes: kvq_plane_bytes.
+ */
+typedef struct kvq_plane {
+    int32_t codec;              /* kvq_codec (ignored for LOWRANK) */
+    int32_t basis;              /* kvq_basis */
+    void *codes;
+    uint16_t *scales;
+    uint16_t *mins;
+    uint16_t *tail;
+    const float *w;             /* HADAMARD: [Hkv][128] binary32 1/sigma */
+    const uint16_t *proj;       /* LOWRANK: [Hkv][128][128] binary16, head h
+                                   uses columns [0, rank[h]) */
+    const int32_t *rank;        /* LOWRANK, host [Hkv]: 16, 32, 64 or 128 */
+    const int32_t *head_codec;  /* LOWRANK, host [Hkv]: kvq_codec of head h
+                                   (_0 or _1; not F16) */
+} kvq_plane;
+
+typedef struct kvq_layer {
+    kvq_plane k, v;
+    int32_t batch;              /* B >= 1 */
+    int32_t n_kv_heads;         /* Hkv >= 1 (<= 32 for LOWRANK) */
+    int32_t head_dim;           /* must be 128 */
+    int32_t capacity;           /* rows per plane, multiple of 64 */
+    int32_t tail_len;           /* N, multiple of 64, 0 = no tail */
+    int32_t n_tokens;           /* T tokens already cached, 0 <= T <= capacity */
+} kvq_layer;
+
+/* Byte sizes of the device buffers of K (which = 0) or V (which = 1):
+ * codes, scales, mins (0 when absent) and tail (0 when tail_len == 0).
+ * Any output pointer may be NULL. */
+kvq_status kvq_plane_bytes(const kvq_layer *layer, int32_t which, size_t *codes_bytes,
+                           size_t *scales_bytes, size_t *mins_bytes, size_t *tail_bytes);
+
+/* Append n_new >= 1 tokens at positions n_tokens .. n_tokens+n_new-1.
+ * k_new, v_new: device binary32 [B][n_new][Hkv][128].  Writes body codes,
+ * scales, mins of every new token and, when tail_len > 0, its binary16 copy
+ * into tail slot t mod tail_len (the newest token wins a slot).  The caller
+ * advances n_tokens afterwards.  KVQ_ERR_CAPACITY if the rows do not fit. */
+kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const float *v_new,
+                               int32_t n_new, void *stream);
+
+/* Re-encode the body rows [0, n_tokens) of K and V from src's codecs to
+ * dst's codecs in the same basis (VBR degrade step), out of place: dst's
+ * codes/scales/mins are written, src is only read, the tails are untouched
+ * (dst may share src's tail buffers).  src and dst must agree on batch,
+ * n_kv_heads, capacity, tail_len, n_tokens, basis and w.  Every codec pair
+ * is accepted; LOWRANK planes are not supported (KVQ_ERR_UNSUPPORTED). */
+kvq_status kvq_transcode_layer(const kvq_layer *src, const kvq_layer *dst, void *stream);
+
+/* Workspace needed by kvq_decode_attention for this layer's shapes and
+ * capacity (independent of n_tokens), in bytes. */
+size_t kvq_decode_workspace_bytes(const kvq_layer *layer, int32_t n_q_heads);
+
+/* Decode attention of one query per head over the first n_tokens tokens.
+ * q: device binary32 [B][n_q_heads][128]; out: device binary32
+ * [B][n_q_heads][128] (raw basis).  Scores are sm_scale * <q, k>.
+ * n_q_heads must be a multiple of n_kv_heads; n_tokens >= 1.  ws: device
+ * scratch of at least kvq_decode_workspace_bytes bytes (contents need no
+ * initialisation and are clobbered).  Tokens t >= n_tokens - tail_len are
+ * read from the tail. */
+kvq_status kvq_decode_attention(const kvq_layer *layer, const float *q, int32_t n_q_heads,
+                                float sm_scale, float *out, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* As kvq_decode_attention with an explicit number of context splits per
+ * (batch, kv head) for the quantised body (0 = the library's choice); the
+ * result does not depend on it beyond floating-point rounding. */
+kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q,
+                                       int32_t n_q_heads, float sm_scale, float *out,
+                                       void *ws, size_t ws_bytes, int32_t body_splits,
+                                       void *stream);
+
+const char *kvq_status_string(kvq_status status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char *kvq_last_error(void);
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

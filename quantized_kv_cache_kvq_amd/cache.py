@@ -1,0 +1,143 @@
+"""A layer of the packed KV cache held in PyTorch device memory.
+
+PyTorch provides the device buffers and the stream; the library's kernels do
+all the work.  The object keeps the host bookkeeping the C ABI leaves to the
+caller: the token count, the per-head tables of the low-rank basis and the
+decode workspace.
+"""
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import torch
+
+from . import lib
+
+
+@dataclass
+class PlaneSpec:
+    """How K or V of a layer is stored."""
+    codec: str = "q8_0"
+    basis: str = "plain"                      # "plain" | "hadamard" | "lowrank"
+    w: Optional[torch.Tensor] = None          # hadamard: [Hkv, 128] float32, 1/sigma
+    proj: Optional[torch.Tensor] = None       # lowrank: [Hkv, 128, 128] float16
+    ranks: Sequence[int] = field(default_factory=tuple)
+    head_codecs: Sequence[str] = field(default_factory=tuple)
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+class LayerCache:
+    def __init__(self, batch, n_kv_heads, capacity, tail_len, kspec: PlaneSpec,
+                 vspec: PlaneSpec, device="cuda", share_tail_with=None):
+        self.device = torch.device(device)
+        self.batch, self.n_kv_heads = batch, n_kv_heads
+        self.capacity, self.tail_len = capacity, tail_len
+        self.kspec, self.vspec = kspec, vspec
+        self.desc = lib.kvq_layer()
+        self.desc.batch, self.desc.n_kv_heads = batch, n_kv_heads
+        self.desc.head_dim, self.desc.capacity = lib.HEAD_DIM, capacity
+        self.desc.tail_len, self.desc.n_tokens = tail_len, 0
+        self._keep = []
+        self.bufs = {}
+        for which, name, spec in ((0, "k", kspec), (1, "v", vspec)):
+            plane = self.desc.k if which == 0 else self.desc.v
+            self._fill_spec(plane, spec)
+            codes, scales, mins, tail = lib.plane_bytes(self.desc, which)
+            b = {
+                "codes": torch.zeros(max(codes, 1), dtype=torch.uint8, device=self.device),
+                "scales": torch.zeros(scales, dtype=torch.uint8, device=self.device) if scales else None,
+                "mins": torch.zeros(mins, dtype=torch.uint8, device=self.device) if mins else None,
+            }
+            if tail:
+                b["tail"] = (share_tail_with.bufs[name]["tail"] if share_tail_with is not None
+                             else torch.zeros(tail, dtype=torch.uint8, device=self.device))
+            else:
+                b["tail"] = None
+            plane.codes = _ptr(b["codes"]).value
+            plane.scales = _ptr(b["scales"]).value
+            plane.mins = _ptr(b["mins"]).value
+            plane.tail = _ptr(b["tail"]).value
+            self.bufs[name] = b
+        self._ws = None
+
+    def _fill_spec(self, plane, spec):
+        plane.basis = lib.BASIS_ID[spec.basis]
+        plane.codec = lib.CODEC_ID[spec.codec] if spec.basis != "lowrank" else 0
+        if spec.basis == "hadamard":
+            w = spec.w.to(self.device, torch.float32).contiguous()
+            self._keep.append(w)
+            plane.w = w.data_ptr()
+        if spec.basis == "lowrank":
+            P = spec.proj.to(self.device, torch.float16).contiguous()
+            self._keep.append(P)
+            plane.proj = P.data_ptr()
+            ranks = (ctypes.c_int32 * self.n_kv_heads)(*spec.ranks)
+            hc = (ctypes.c_int32 * self.n_kv_heads)(*[lib.CODEC_ID[c] for c in spec.head_codecs])
+            self._keep += [ranks, hc]
+            plane.rank = ctypes.cast(ranks, ctypes.POINTER(ctypes.c_int32))
+            plane.head_codec = ctypes.cast(hc, ctypes.POINTER(ctypes.c_int32))
+
+    @property
+    def n_tokens(self):
+        return self.desc.n_tokens
+
+    @n_tokens.setter
+    def n_tokens(self, t):
+        self.desc.n_tokens = t
+
+    def append(self, k_new, v_new, stream=None):
+        """k_new, v_new: float32 [B, n, Hkv, 128] on the device."""
+        k_new = k_new.contiguous()
+        v_new = v_new.contiguous()
+        if k_new.dtype != torch.float32 or k_new.shape != v_new.shape or k_new.dim() != 4:
+            raise ValueError("k_new/v_new must be float32 [B, n, Hkv, 128] of equal shape")
+        if k_new.shape[0] != self.batch or k_new.shape[2] != self.n_kv_heads or k_new.shape[3] != 128:
+            raise ValueError("k_new shape %s does not match the layer" % (tuple(k_new.shape),))
+        n = k_new.shape[1]
+        lib.quantize_append(self.desc, _ptr(k_new), _ptr(v_new), n, _stream(self.device, stream))
+        self.desc.n_tokens += n
+
+    def workspace(self, n_q_heads):
+        need = lib.decode_workspace_bytes(self.desc, n_q_heads)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode(self, q, sm_scale, out=None, body_splits=0, stream=None, ws=None):
+        """q: float32 [B, Hq, 128] -> out float32 [B, Hq, 128]."""
+        q = q.contiguous()
+        if q.dtype != torch.float32 or q.dim() != 3 or q.shape[0] != self.batch or q.shape[2] != 128:
+            raise ValueError("q must be float32 [B, Hq, 128]")
+        Hq = q.shape[1]
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(Hq) if ws is None else ws
+        lib.decode_attention(self.desc, _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(ws),
+                             ws.numel(), _stream(self.device, stream), body_splits)
+        return out
+
+    def transcode(self, kcodec, vcodec, stream=None):
+        """A new layer with K and V re-encoded; shares this layer's tails."""
+        ks = PlaneSpec(kcodec, self.kspec.basis, self.kspec.w)
+        vs = PlaneSpec(vcodec, self.vspec.basis, self.vspec.w)
+        dst = LayerCache(self.batch, self.n_kv_heads, self.capacity, self.tail_len, ks, vs,
+                         self.device, share_tail_with=self)
+        dst.n_tokens = self.n_tokens
+        lib.transcode_layer(self.desc, dst.desc, _stream(self.device, stream))
+        return dst
+
+    def transcode_into(self, dst, stream=None):
+        """Re-encode into an existing layer ``dst`` (same shapes and token count)."""
+        dst.n_tokens = self.n_tokens
+        lib.transcode_layer(self.desc, dst.desc, _stream(self.device, stream))
+        return dst

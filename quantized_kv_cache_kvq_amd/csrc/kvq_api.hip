@@ -1,0 +1,399 @@
+// C ABI of libkvq.so: argument checks, plans and dispatch to the kernels.
+// Every check runs on the host before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "kvq_common.hpp"
+#include "kvq_internal.hpp"
+
+using namespace kvq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kvq_status ok() {
+  g_err[0] = '\0';
+  return KVQ_OK;
+}
+
+kvq_status hip_fail(hipError_t e, const char *what) {
+  return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool codec_ok(int c) { return c >= 0 && c < KVQ_NUM_CODECS; }
+
+// Checks one plane of a layer; `name` is "k" or "v".
+kvq_status check_plane(const kvq_layer &L, const kvq_plane &p, const char *name) {
+  if (p.basis < KVQ_BASIS_PLAIN || p.basis > KVQ_BASIS_LOWRANK)
+    return fail(KVQ_ERR_INVALID_ARG, "%s.basis %d is not a kvq_basis", name, p.basis);
+  if (p.codes == nullptr) return fail(KVQ_ERR_INVALID_ARG, "%s.codes is NULL", name);
+  if (L.tail_len > 0 && p.tail == nullptr)
+    return fail(KVQ_ERR_INVALID_ARG, "%s.tail is NULL with tail_len %d", name, L.tail_len);
+  bool any_q = false, any_1 = false;
+  if (p.basis == KVQ_BASIS_LOWRANK) {
+    if (L.n_kv_heads > KVQ_MAX_LOWRANK_HEADS)
+      return fail(KVQ_ERR_UNSUPPORTED, "low-rank planes support at most %d kv heads",
+                  KVQ_MAX_LOWRANK_HEADS);
+    if (!p.proj || !p.rank || !p.head_codec)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: low-rank plane needs proj, rank and head_codec", name);
+    for (int h = 0; h < L.n_kv_heads; ++h) {
+      const int r = p.rank[h], c = p.head_codec[h];
+      if (!(r == 16 || r == 32 || r == 64 || r == 128))
+        return fail(KVQ_ERR_INVALID_ARG, "%s.rank[%d] = %d (must be 16, 32, 64 or 128)", name, h, r);
+      if (!codec_ok(c) || c == KVQ_F16)
+        return fail(KVQ_ERR_INVALID_ARG, "%s.head_codec[%d] = %d is not a block codec", name, h, c);
+      any_q = true;
+      any_1 = any_1 || codec_family(c) == FAM_1;
+    }
+  } else {
+    if (!codec_ok(p.codec))
+      return fail(KVQ_ERR_INVALID_ARG, "%s.codec %d is not a kvq_codec", name, p.codec);
+    any_q = p.codec != KVQ_F16;
+    any_1 = codec_family(p.codec) == FAM_1;
+    if (p.basis == KVQ_BASIS_HADAMARD && p.w == nullptr)
+      return fail(KVQ_ERR_INVALID_ARG, "%s.w is NULL for the Hadamard basis", name);
+  }
+  if (any_q && p.scales == nullptr) return fail(KVQ_ERR_INVALID_ARG, "%s.scales is NULL", name);
+  if (any_1 && p.mins == nullptr) return fail(KVQ_ERR_INVALID_ARG, "%s.mins is NULL", name);
+  return KVQ_OK;
+}
+
+kvq_status check_layer(const kvq_layer *L) {
+  if (!L) return fail(KVQ_ERR_INVALID_ARG, "layer is NULL");
+  if (L->head_dim != KVQ_HEAD_DIM)
+    return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d (only %d is supported)", L->head_dim, KVQ_HEAD_DIM);
+  if (L->batch < 1 || L->n_kv_heads < 1)
+    return fail(KVQ_ERR_INVALID_ARG, "batch %d and n_kv_heads %d must be >= 1", L->batch, L->n_kv_heads);
+  if (L->capacity < 0 || L->capacity % KVQ_TILE_TOKENS)
+    return fail(KVQ_ERR_INVALID_ARG, "capacity %d must be a non-negative multiple of %d",
+                L->capacity, KVQ_TILE_TOKENS);
+  if (L->tail_len < 0 || L->tail_len % KVQ_TILE_TOKENS)
+    return fail(KVQ_ERR_INVALID_ARG, "tail_len %d must be a non-negative multiple of %d",
+                L->tail_len, KVQ_TILE_TOKENS);
+  if (L->n_tokens < 0 || L->n_tokens > L->capacity)
+    return fail(KVQ_ERR_INVALID_ARG, "n_tokens %d outside [0, capacity %d]", L->n_tokens, L->capacity);
+  kvq_status s = check_plane(*L, L->k, "k");
+  if (s != KVQ_OK) return s;
+  s = check_plane(*L, L->v, "v");
+  if (s != KVQ_OK) return s;
+  if ((L->k.basis == KVQ_BASIS_LOWRANK) != (L->v.basis == KVQ_BASIS_LOWRANK))
+    return fail(KVQ_ERR_UNSUPPORTED, "K and V must both or neither use the low-rank basis");
+  if (L->k.basis == KVQ_BASIS_LOWRANK) {
+    for (int h = 0; h < L->n_kv_heads; ++h)
+      if (L->k.rank[h] != L->v.rank[h] || L->k.head_codec[h] != L->v.head_codec[h])
+        return fail(KVQ_ERR_UNSUPPORTED, "low-rank head %d: K and V must share rank and codec", h);
+  }
+  return KVQ_OK;
+}
+
+PlaneArgs plane_args(const kvq_layer &L, const kvq_plane &p) {
+  PlaneArgs a;
+  memset(&a, 0, sizeof a);
+  a.codes = reinterpret_cast<uint8_t *>(p.codes);
+  a.scales = p.scales;
+  a.mins = p.mins;
+  a.tail = p.tail;
+  a.w = p.w;
+  a.proj = p.proj;
+  a.codec = p.codec;
+  a.basis = p.basis;
+  a.hkv = L.n_kv_heads;
+  a.capacity = L.capacity;
+  a.tail_len = L.tail_len;
+  if (p.basis == KVQ_BASIS_LOWRANK) {
+    for (int h = 0; h < L.n_kv_heads; ++h) {
+      a.hcodec[h] = (int8_t)p.head_codec[h];
+      a.hrank[h] = (int16_t)p.rank[h];
+    }
+    a.codec = -1;
+  }
+  return a;
+}
+
+void plane_sizes(const kvq_layer &L, const kvq_plane &p, size_t &codes, size_t &scales,
+                 size_t &mins, size_t &tail) {
+  codes = scales = mins = 0;
+  const size_t cap = (size_t)L.capacity;
+  if (p.basis == KVQ_BASIS_LOWRANK) {
+    for (int h = 0; h < L.n_kv_heads; ++h) {
+      const int r = p.rank[h], c = p.head_codec[h];
+      codes += cap * row_bytes(c, r);
+      scales += cap * (r / block_len(r)) * 2;
+      if (codec_family(c) == FAM_1) mins += cap * (r / block_len(r)) * 2;
+    }
+    codes *= L.batch;
+    scales *= L.batch;
+    mins *= L.batch;
+  } else {
+    const size_t planes = (size_t)L.batch * L.n_kv_heads;
+    codes = planes * cap * row_bytes(p.codec, KVQ_HEAD_DIM);
+    if (p.codec != KVQ_F16) scales = planes * cap * (KVQ_HEAD_DIM / 32) * 2;
+    if (codec_family(p.codec) == FAM_1) mins = scales;
+  }
+  tail = (size_t)L.batch * L.n_kv_heads * L.tail_len * 2 * KVQ_HEAD_DIM;
+}
+
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int MAX_BODY_SPLITS = 1024;
+constexpr int MAX_TAIL_SPLITS = 64;
+constexpr int TAIL_TT = 128;
+
+int max_splits(const kvq_layer &L) {
+  const int tt = decode_tile_tokens(L.k.codec, L.v.codec, L.k.basis);
+  int body = (L.capacity + tt - 1) / tt;
+  if (body > MAX_BODY_SPLITS) body = MAX_BODY_SPLITS;
+  int tail = (L.tail_len + TAIL_TT - 1) / TAIL_TT;
+  if (tail > MAX_TAIL_SPLITS) tail = MAX_TAIL_SPLITS;
+  return (body > 0 ? body : 1) + tail;
+}
+
+struct WsLayout {
+  size_t qw, qsum, part, total;
+};
+
+WsLayout ws_layout(const kvq_layer &L, int Hq, int S) {
+  WsLayout w;
+  const size_t bh = (size_t)L.batch * Hq;
+  w.qw = 0;
+  w.qsum = align256(bh * KVQ_HEAD_DIM * sizeof(float));
+  w.part = w.qsum + align256(bh * 4 * sizeof(float));
+  w.total = w.part + align256(bh * (size_t)S * PSTRIDE * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char *kvq_last_error(void) { return g_err; }
+
+const char *kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_CAPACITY: return "KVQ_ERR_CAPACITY";
+    case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE";
+    case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+  }
+  return "KVQ_ERR_UNKNOWN";
+}
+
+kvq_status kvq_plane_bytes(const kvq_layer *layer, int32_t which, size_t *codes_bytes,
+                           size_t *scales_bytes, size_t *mins_bytes, size_t *tail_bytes) {
+  kvq_status s = check_layer(layer);
+  if (s != KVQ_OK && s != KVQ_ERR_INVALID_ARG) return s;
+  if (!layer) return s;
+  // sizes only need shapes, codecs and (low rank) the host tables
+  if (which != 0 && which != 1) return fail(KVQ_ERR_INVALID_ARG, "which must be 0 (K) or 1 (V)");
+  const kvq_plane &p = which ? layer->v : layer->k;
+  if (layer->head_dim != KVQ_HEAD_DIM || layer->batch < 1 || layer->n_kv_heads < 1 ||
+      layer->capacity < 0 || layer->capacity % KVQ_TILE_TOKENS || layer->tail_len < 0 ||
+      layer->tail_len % KVQ_TILE_TOKENS)
+    return fail(KVQ_ERR_INVALID_ARG, "bad layer shape");
+  if (p.basis == KVQ_BASIS_LOWRANK) {
+    if (!p.rank || !p.head_codec || layer->n_kv_heads > KVQ_MAX_LOWRANK_HEADS)
+      return fail(KVQ_ERR_INVALID_ARG, "low-rank plane needs rank and head_codec tables");
+    for (int h = 0; h < layer->n_kv_heads; ++h) {
+      const int r = p.rank[h], c = p.head_codec[h];
+      if (!(r == 16 || r == 32 || r == 64 || r == 128) || !codec_ok(c) || c == KVQ_F16)
+        return fail(KVQ_ERR_INVALID_ARG, "low-rank head %d: bad rank %d or codec %d", h, r, c);
+    }
+  } else if (!codec_ok(p.codec)) {
+    return fail(KVQ_ERR_INVALID_ARG, "codec %d is not a kvq_codec", p.codec);
+  }
+  size_t c, sc, m, t;
+  plane_sizes(*layer, p, c, sc, m, t);
+  if (codes_bytes) *codes_bytes = c;
+  if (scales_bytes) *scales_bytes = sc;
+  if (mins_bytes) *mins_bytes = m;
+  if (tail_bytes) *tail_bytes = t;
+  return ok();
+}
+
+kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const float *v_new,
+                               int32_t n_new, void *stream) {
+  kvq_status s = check_layer(layer);
+  if (s != KVQ_OK) return s;
+  if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  if (n_new < 1) return fail(KVQ_ERR_INVALID_ARG, "n_new %d must be >= 1", n_new);
+  if ((long long)layer->n_tokens + n_new > layer->capacity)
+    return fail(KVQ_ERR_CAPACITY, "n_tokens %d + n_new %d exceeds capacity %d", layer->n_tokens,
+                n_new, layer->capacity);
+  if ((long long)layer->batch * n_new * layer->n_kv_heads * 2 > 0x7fffffffLL)
+    return fail(KVQ_ERR_UNSUPPORTED, "append too large for one launch; split n_new");
+  const PlaneArgs kp = plane_args(*layer, layer->k), vp = plane_args(*layer, layer->v);
+  hipError_t e = launch_append(kp, vp, k_new, v_new, layer->batch, n_new, layer->n_tokens,
+                               reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+kvq_status kvq_transcode_layer(const kvq_layer *src, const kvq_layer *dst, void *stream) {
+  kvq_status s = check_layer(src);
+  if (s != KVQ_OK) return s;
+  s = check_layer(dst);
+  if (s != KVQ_OK) return s;
+  if (src->batch != dst->batch || src->n_kv_heads != dst->n_kv_heads ||
+      src->capacity != dst->capacity || src->tail_len != dst->tail_len ||
+      src->n_tokens != dst->n_tokens)
+    return fail(KVQ_ERR_INVALID_ARG, "src and dst layers differ in shape or n_tokens");
+  if (src->k.basis != dst->k.basis || src->v.basis != dst->v.basis)
+    return fail(KVQ_ERR_INVALID_ARG, "transcode keeps the basis: src and dst bases differ");
+  if (src->k.basis == KVQ_BASIS_LOWRANK || src->v.basis == KVQ_BASIS_LOWRANK)
+    return fail(KVQ_ERR_UNSUPPORTED, "transcode of low-rank planes is not supported");
+  if (src->k.codes == dst->k.codes || src->v.codes == dst->v.codes)
+    return fail(KVQ_ERR_INVALID_ARG, "transcode is out of place: src and dst codes alias");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  for (int which = 0; which < 2; ++which) {
+    const kvq_plane &ps = which ? src->v : src->k;
+    const kvq_plane &pd = which ? dst->v : dst->k;
+    hipError_t e = launch_transcode(plane_args(*src, ps), plane_args(*dst, pd), src->batch,
+                                    src->n_tokens, st);
+    if (e != hipSuccess) return hip_fail(e, "transcode launch");
+  }
+  return ok();
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_layer *layer, int32_t n_q_heads) {
+  if (!layer || n_q_heads < 1 || layer->batch < 1) return 0;
+  if (layer->capacity < 0 || layer->tail_len < 0) return 0;
+  return ws_layout(*layer, n_q_heads, max_splits(*layer)).total;
+}
+
+kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, int32_t n_q_heads,
+                                       float sm_scale, float *out, void *ws, size_t ws_bytes,
+                                       int32_t body_splits, void *stream) {
+  kvq_status s = check_layer(layer);
+  if (s != KVQ_OK) return s;
+  const kvq_layer &L = *layer;
+  if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q / out is NULL");
+  if (n_q_heads < 1 || n_q_heads % L.n_kv_heads)
+    return fail(KVQ_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                n_q_heads, L.n_kv_heads);
+  if (L.n_tokens < 1) return fail(KVQ_ERR_INVALID_ARG, "decode needs n_tokens >= 1");
+  if (body_splits < 0) return fail(KVQ_ERR_INVALID_ARG, "body_splits %d < 0", body_splits);
+  if (L.k.basis != L.v.basis)
+    return fail(KVQ_ERR_UNSUPPORTED, "decode needs K and V in the same basis");
+
+  DecodePlan P;
+  P.B = L.batch;
+  P.Hkv = L.n_kv_heads;
+  P.Hq = n_q_heads;
+  P.G = n_q_heads / L.n_kv_heads;
+  P.HG = decode_head_group(P.G);
+  P.NHG = P.G / P.HG;
+  P.T = L.n_tokens;
+  P.tail_tokens = L.tail_len < P.T ? L.tail_len : P.T;
+  P.body_tokens = P.T - P.tail_tokens;
+  if (L.k.basis == KVQ_BASIS_LOWRANK) {
+    for (int h = 0; h < L.n_kv_heads; ++h)
+      if (!decode_lowrank_supported(L.k.head_codec[h], L.k.rank[h]))
+        return fail(KVQ_ERR_UNSUPPORTED, "low-rank head %d: codec %d at rank %d not supported by decode",
+                    h, L.k.head_codec[h], L.k.rank[h]);
+  } else if (!decode_pair_supported(L.k.codec, L.v.codec, P.HG)) {
+    return fail(KVQ_ERR_UNSUPPORTED, "decode of K codec %d with V codec %d (group %d) not supported",
+                L.k.codec, L.v.codec, P.HG);
+  }
+  P.tt_body = decode_tile_tokens(L.k.codec, L.v.codec, L.k.basis);
+  const int units = P.B * P.Hkv * P.NHG;
+  const int body_tiles = (P.body_tokens + P.tt_body - 1) / P.tt_body;
+  if (body_tiles > 0) {
+    int want = body_splits;
+    if (want == 0) {
+      const int target = 2 * device_cus();
+      want = (target + units - 1) / units;
+    }
+    if (want > MAX_BODY_SPLITS) want = MAX_BODY_SPLITS;
+    if (want > body_tiles) want = body_tiles;
+    if (want < 1) want = 1;
+    P.tiles_per_split_body = (body_tiles + want - 1) / want;
+    P.S_body = (body_tiles + P.tiles_per_split_body - 1) / P.tiles_per_split_body;
+  } else {
+    P.tiles_per_split_body = 1;
+    P.S_body = 0;
+  }
+  const int tail_tiles = (P.tail_tokens + TAIL_TT - 1) / TAIL_TT;
+  if (tail_tiles > 0) {
+    int want = tail_tiles < MAX_TAIL_SPLITS ? tail_tiles : MAX_TAIL_SPLITS;
+    P.tiles_per_split_tail = (tail_tiles + want - 1) / want;
+    P.S_tail = (tail_tiles + P.tiles_per_split_tail - 1) / P.tiles_per_split_tail;
+  } else {
+    P.tiles_per_split_tail = 1;
+    P.S_tail = 0;
+  }
+  P.S_total = P.S_body + P.S_tail;
+  P.prep = L.k.basis != KVQ_BASIS_PLAIN || codec_family(L.k.codec) == FAM_1;
+  P.qsum = true;
+
+  const WsLayout W = ws_layout(L, n_q_heads, P.S_total);
+  if (!ws) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < W.total)
+    return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, W.total);
+  if ((long long)units * P.S_total > 0x7fffffffLL)
+    return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+
+  uint8_t *wsb = reinterpret_cast<uint8_t *>(ws);
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.k = plane_args(L, L.k);
+  a.v = plane_args(L, L.v);
+  a.part = reinterpret_cast<float *>(wsb + W.part);
+  a.B = P.B;
+  a.Hkv = P.Hkv;
+  a.Hq = P.Hq;
+  a.G = P.G;
+  a.HG = P.HG;
+  a.NHG = P.NHG;
+  a.body_tokens = P.body_tokens;
+  a.tail_tokens = P.tail_tokens;
+  a.S_body = P.S_body;
+  a.S_tail = P.S_tail;
+  a.S_total = P.S_total;
+  a.tps_body = P.tiles_per_split_body;
+  a.tps_tail = P.tiles_per_split_tail;
+  a.tt_body = P.tt_body;
+  hipError_t e = launch_decode(a, q, sm_scale, reinterpret_cast<float *>(wsb + W.qw),
+                               reinterpret_cast<float *>(wsb + W.qsum), out,
+                               reinterpret_cast<hipStream_t>(stream), P.prep, P.qsum);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+kvq_status kvq_decode_attention(const kvq_layer *layer, const float *q, int32_t n_q_heads,
+                                float sm_scale, float *out, void *ws, size_t ws_bytes,
+                                void *stream) {
+  return kvq_decode_attention_splits(layer, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream);
+}
+
+}  // extern "C"

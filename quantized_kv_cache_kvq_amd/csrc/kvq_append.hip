@@ -1,0 +1,191 @@
+// Append kernel: rotate / project, block-quantise, bit-pack and store new
+// tokens, plus their binary16 precision-tail copy.
+//
+// One wave (64 lanes) per (batch entry, new token, kv head, K|V).  Lane l
+// owns raw channels 2l, 2l+1.  Steps, after the BeeLlama v0.4.0 notes (KVarN
+// and precision-tail sections) and the KV-COBRA explainer (projection with
+// the Hadamard rotation fused in):
+//   1. tail copy: RN16 of the raw vector into ring slot t mod tail_len;
+//   2. stored coordinates: x (plain), H (x * w) by an in-wave fast
+//      Walsh-Hadamard transform (hadamard), or P_h^T x (low rank);
+//   3. per 32-block (or min(32, rank) block) scale (and min);
+//   4. codes with correctly rounded binary32 division and rint (ties even):
+//      this reproduces the exact-quotient definition bit for bit;
+//   5. bit-pack the row and store it in the 64-token tiled layout.
+#include "kvq_common.hpp"
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+// In-wave fast Walsh-Hadamard transform of 128 values, lane l holding
+// elements 2l (a) and 2l+1 (b).  Butterflies (u+v, u-v) at every stride give
+// the Sylvester (natural-order) H applied to the vector.
+__device__ inline void fwht128_wave(float &a, float &b) {
+  const int lane = threadIdx.x & 63;
+  float s = a + b, d = a - b;          // stride 1: inside the lane
+  a = s;
+  b = d;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {   // stride 2m: partner lane l ^ m
+    float pa = __shfl_xor(a, m, 64);
+    float pb = __shfl_xor(b, m, 64);
+    bool upper = (lane & m) != 0;
+    a = upper ? (pa - a) : (a + pa);
+    b = upper ? (pb - b) : (b + pb);
+  }
+}
+
+__global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
+                                                    const float *__restrict__ k_new,
+                                                    const float *__restrict__ v_new, int n_new,
+                                                    int t0) {
+  __shared__ float xin[D];
+  __shared__ float coords[D];
+  __shared__ uint8_t codes[D];
+  __shared__ float s_scale[4];
+  __shared__ float s_min[4];
+
+  int id = blockIdx.x;
+  const int which = id & 1;
+  id >>= 1;
+  const PlaneArgs &p = which ? vp : kp;
+  const int hkv = p.hkv;
+  const int h = id % hkv;
+  id /= hkv;
+  const int i = id % n_new;
+  const int b = id / n_new;
+  const int t = t0 + i;
+  const int lane = threadIdx.x;
+
+  const float *src = (which ? v_new : k_new) + (((long long)b * n_new + i) * hkv + h) * D;
+  float2 x = reinterpret_cast<const float2 *>(src)[lane];
+
+  // 1. precision tail: binary16 raw copy, slot t mod N, 256-byte rows.  Only
+  //    the newest N tokens of this call write: older ones in the same call
+  //    would race for the slots they share with newer ones.
+  if (p.tail_len > 0 && i + p.tail_len >= n_new) {
+    const long long plane = (long long)b * hkv + h;
+    const int slot = t % p.tail_len;
+    uint32_t pair = (uint32_t)f32_to_f16_bits(x.x) | ((uint32_t)f32_to_f16_bits(x.y) << 16);
+    uint8_t *base = reinterpret_cast<uint8_t *>(p.tail) + plane * p.tail_len * (2 * D);
+    const int byte = 4 * lane;
+    *reinterpret_cast<uint32_t *>(base + tiled_offset(slot, byte / 16, 2 * D, 16) + byte % 16) = pair;
+  }
+
+  const HeadGeom g = head_geom(p, b, h);
+
+  // 2. stored coordinates
+  if (p.basis == KVQ_BASIS_HADAMARD) {
+    const float *w = p.w + (long long)h * D;
+    float a = x.x * w[2 * lane];
+    float c = x.y * w[2 * lane + 1];
+    fwht128_wave(a, c);
+    coords[2 * lane] = a;
+    coords[2 * lane + 1] = c;
+  } else if (p.basis == KVQ_BASIS_LOWRANK) {
+    xin[2 * lane] = x.x;
+    xin[2 * lane + 1] = x.y;
+    __syncthreads();
+    const uint16_t *P = p.proj + (long long)h * D * D;
+    for (int k = lane; k < g.n; k += 64) {
+      float acc = 0.f;
+      for (int r = 0; r < D; ++r) acc = fmaf(f16_bits_to_f32(P[r * D + k]), xin[r], acc);
+      coords[k] = acc;
+    }
+  } else {
+    coords[2 * lane] = x.x;
+    coords[2 * lane + 1] = x.y;
+  }
+  __syncthreads();
+
+  uint8_t *row_codes = p.codes + g.codes_off;
+  const int fam = codec_family(g.codec);
+  if (fam == FAM_F16) {
+    // binary16 row: dword `lane` holds coordinates 2*lane, 2*lane+1
+    uint32_t pair = (uint32_t)f32_to_f16_bits(coords[2 * lane]) |
+                    ((uint32_t)f32_to_f16_bits(coords[2 * lane + 1]) << 16);
+    const int byte = 4 * lane;
+    *reinterpret_cast<uint32_t *>(row_codes + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c) = pair;
+    return;
+  }
+
+  const int bits = codec_bits(g.codec);
+  // 3. block scale (and min), one lane per block
+  if (lane < g.nblk) {
+    const float *blk = coords + lane * g.L;
+    const long long so = g.scales_off + (long long)t * g.nblk + lane;
+    if (fam == FAM_0) {
+      float amax = 0.f;
+      for (int e = 0; e < g.L; ++e) amax = fmaxf(amax, fabsf(blk[e]));
+      const float qmax = (float)((1 << (bits - 1)) - 1);
+      uint16_t dh = f32_to_f16_bits(amax / qmax);
+      p.scales[so] = dh;
+      s_scale[lane] = f16_bits_to_f32(dh);
+    } else {
+      float lo = blk[0], hi = blk[0];
+      for (int e = 1; e < g.L; ++e) {
+        lo = fminf(lo, blk[e]);
+        hi = fmaxf(hi, blk[e]);
+      }
+      uint16_t mh = f32_to_f16_bits(lo);
+      const float m = f16_bits_to_f32(mh);
+      const float R = hi - m;
+      const float levels = (float)((1 << bits) - 1);
+      uint16_t dh = f32_to_f16_bits(R / levels);
+      p.scales[so] = dh;
+      p.mins[so] = mh;
+      s_scale[lane] = f16_bits_to_f32(dh);
+      s_min[lane] = m;
+    }
+  }
+  __syncthreads();
+
+  // 4. codes (masked to `bits` bits)
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int e = lane; e < g.n; e += 64) {
+    const int j = e / g.L;
+    const float d = s_scale[j];
+    int q = 0;
+    if (fam == FAM_0) {
+      const float qmax = (float)((1 << (bits - 1)) - 1);
+      if (d != 0.f) q = (int)fminf(fmaxf(rintf(coords[e] / d), -qmax), qmax);
+    } else {
+      const float levels = (float)((1 << bits) - 1);
+      const float y = coords[e] - s_min[j];
+      if (d != 0.f) q = (int)fminf(fmaxf(rintf(y / d), 0.f), levels);
+    }
+    codes[e] = (uint8_t)((uint32_t)q & mask);
+  }
+  __syncthreads();
+
+  // 5. pack: unit u (us bytes) holds row bits [8*us*u, 8*us*(u+1))
+  const int us = g.c < 4 ? g.c : 4;
+  const int nunits = g.R / us;
+  if (lane < nunits) {
+    const int bit0 = 8 * us * lane, bit1 = bit0 + 8 * us;
+    uint64_t acc = 0;
+    for (int e = bit0 / bits; e < g.n && e * bits < bit1; ++e) {
+      const int sh = e * bits - bit0;
+      const uint64_t v = codes[e];
+      acc |= sh >= 0 ? (v << sh) : (v >> (-sh));
+    }
+    const int byte = us * lane;
+    uint8_t *dst = row_codes + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c;
+    if (us == 4)
+      *reinterpret_cast<uint32_t *>(dst) = (uint32_t)acc;
+    else if (us == 2)
+      *reinterpret_cast<uint16_t *>(dst) = (uint16_t)acc;
+    else
+      *dst = (uint8_t)acc;
+  }
+}
+
+hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
+                         const float *v_new, int batch, int n_new, int t0, hipStream_t stream) {
+  const long long blocks = (long long)batch * n_new * kp.hkv * 2;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, kp, vp, k_new,
+                     v_new, n_new, t0);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,6 @@
+// Decode kernels instantiated for 2 query head(s) per workgroup.
+#include "kvq_decode_impl.hpp"
+
+namespace kvq {
+template hipError_t launch_decode_hg<2>(const DecodeArgs &, dim3, hipStream_t);
+}  // namespace kvq

@@ -1,0 +1,54 @@
+// Internal host-side interface between the C ABI and the kernel launchers.
+#pragma once
+
+#include "kvq_common.hpp"
+
+namespace kvq {
+
+// Partial result of one context split for one query head:
+// {m (log2 domain), l, pad, pad, o[128]}.
+constexpr int PSTRIDE = 132;
+
+struct DecodePlan {
+  int B, Hkv, Hq, G, HG, NHG;     // HG heads per workgroup, NHG = G / HG
+  int T, body_tokens, tail_tokens;
+  int tt_body;                    // tokens per workgroup tile of the body
+  int S_body, S_tail, S_total;    // context splits per (b, kv head, head group)
+  int tiles_per_split_body, tiles_per_split_tail;
+  bool prep;                      // query pre-transform needed
+  bool qsum;                      // per-block query sums needed (_1 keys)
+};
+
+struct DecodeArgs {
+  PlaneArgs k, v;
+  const float *q_body;    // [B][Hq][128] (raw query, or pre-transformed)
+  const float *q_tail;    // [B][Hq][128] raw query
+  const float *qsum;      // [B][Hq][4] per-block query sums (_1 keys)
+  float scale_body;       // multiplier taking body scores to the log2 domain
+  float scale_tail;
+  float *part;            // [B][Hq][S_total][PSTRIDE]
+  int B, Hkv, Hq, G, HG, NHG;
+  int body_tokens, tail_tokens;
+  int S_body, S_tail, S_total;
+  int tps_body, tps_tail;
+  int tt_body;
+};
+
+hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
+                         const float *v_new, int batch, int n_new, int t0, hipStream_t stream);
+
+hipError_t launch_transcode(const PlaneArgs &src, const PlaneArgs &dst, int batch, int T,
+                            hipStream_t stream);
+
+hipError_t launch_decode(const DecodeArgs &a, const float *q, float sm_scale, float *qw,
+                         float *qsum, float *out, hipStream_t stream, bool prep, bool need_qsum);
+
+int decode_tile_tokens(int kcodec, int vcodec, int basis);
+int decode_head_group(int G);
+bool decode_lowrank_supported(int codec, int rank);
+bool decode_pair_supported(int kcodec, int vcodec, int hg);
+
+template <int HG>
+hipError_t launch_decode_hg(const DecodeArgs &a, dim3 grid, hipStream_t st);
+
+}  // namespace kvq

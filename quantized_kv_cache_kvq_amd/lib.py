@@ -1,0 +1,143 @@
+"""ctypes binding of libkvq.so: the C structs and entry points of
+``include/kvq.h`` with the same names.  Argument marshalling only; every step
+of the computation runs in the library's HIP kernels.
+
+``load()`` raises if the library has not been built: there is no fallback.
+"""
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "kvq.h")
+
+KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(6)
+
+CODECS = ["f16", "q8_0", "q6_0", "q5_0", "q4_0", "q3_0", "q2_0",
+          "q8_1", "q6_1", "q5_1", "q4_1", "q3_1", "q2_1", "q1_1"]
+CODEC_ID = {n: i for i, n in enumerate(CODECS)}
+BASIS_ID = {"plain": 0, "hadamard": 1, "lowrank": 2}
+HEAD_DIM = 128
+TILE = 64
+
+
+class kvq_plane(ctypes.Structure):
+    _fields_ = [
+        ("codec", ctypes.c_int32),
+        ("basis", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("mins", ctypes.c_void_p),
+        ("tail", ctypes.c_void_p),
+        ("w", ctypes.c_void_p),
+        ("proj", ctypes.c_void_p),
+        ("rank", ctypes.POINTER(ctypes.c_int32)),
+        ("head_codec", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class kvq_layer(ctypes.Structure):
+    _fields_ = [
+        ("k", kvq_plane),
+        ("v", kvq_plane),
+        ("batch", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("tail_len", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int32),
+    ]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__("%s: %s" % (_STATUS_NAMES.get(status, status), detail))
+
+
+_STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED",
+                 3: "KVQ_ERR_CAPACITY", 4: "KVQ_ERR_WORKSPACE", 5: "KVQ_ERR_HIP"}
+
+_lib = None
+
+_SIGS = {
+    "kvq_plane_bytes": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
+                                       ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "kvq_quantize_append": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int32, ctypes.c_void_p]),
+    "kvq_transcode_layer": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.POINTER(kvq_layer),
+                                           ctypes.c_void_p]),
+    "kvq_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kvq_layer), ctypes.c_int32]),
+    "kvq_decode_attention": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "kvq_decode_attention_splits": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p,
+                                                   ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                                   ctypes.c_void_p]),
+    "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvq_last_error": (ctypes.c_char_p, []),
+    "kvq_abi_version": (ctypes.c_int32, []),
+}
+
+
+def load(path=LIB_PATH):
+    """Load libkvq.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libkvq.so is not built (%s); run __graft_entry__.build() or "
+                           "python -m quantized_kv_cache_kvq_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.kvq_abi_version() != 1:
+        raise RuntimeError("libkvq.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def header_functions(path=HEADER):
+    """Names of the entry points declared in include/kvq.h."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def check(status):
+    """Raise KvqError for a non-zero kvq_status."""
+    if status != KVQ_OK:
+        detail = load().kvq_last_error().decode()
+        raise KvqError(status, detail)
+
+
+def plane_bytes(layer, which):
+    lib = load()
+    sizes = [ctypes.c_size_t() for _ in range(4)]
+    check(lib.kvq_plane_bytes(ctypes.byref(layer), which, *[ctypes.byref(s) for s in sizes]))
+    return tuple(s.value for s in sizes)
+
+
+def quantize_append(layer, k_new_ptr, v_new_ptr, n_new, stream):
+    check(load().kvq_quantize_append(ctypes.byref(layer), k_new_ptr, v_new_ptr, n_new, stream))
+
+
+def transcode_layer(src, dst, stream):
+    check(load().kvq_transcode_layer(ctypes.byref(src), ctypes.byref(dst), stream))
+
+
+def decode_workspace_bytes(layer, n_q_heads):
+    return load().kvq_decode_workspace_bytes(ctypes.byref(layer), n_q_heads)
+
+
+def decode_attention(layer, q_ptr, n_q_heads, sm_scale, out_ptr, ws_ptr, ws_bytes, stream,
+                     body_splits=0):
+    check(load().kvq_decode_attention_splits(ctypes.byref(layer), q_ptr, n_q_heads,
+                                             ctypes.c_float(sm_scale), out_ptr, ws_ptr, ws_bytes,
+                                             body_splits, stream))

@@ -1,0 +1,165 @@
+"""Shared helpers of the GPU parity tests: matched library/oracle plane
+specifications for a workload, upload of oracle-packed caches, download and
+comparison of device planes.
+
+Acceptance rules (stated once here, used by every parity test):
+* unrotated formats: codes, scales, mins and the tail are bit-exact;
+* rotated (Hadamard) and low-rank codes: at most 0.1% of codes may differ,
+  each by +-1 and only where the exact stored coordinate is within the
+  device's binary32 rounding error of a rounding boundary; a block scale (or
+  min) may differ by one binary16 step only where the exact unrounded value
+  is within that error of a binary16 rounding midpoint, and the codes are
+  then checked against the device's scale;
+* attention outputs: max-abs difference <= 2e-3 against the oracle run on
+  the same cache.
+"""
+
+import numpy as np
+import torch
+
+import oracle.cobra
+import oracle.layer as OL
+from oracle.codecs import CODECS
+from oracle.layer import PlaneSpec as OSpec
+from quantized_kv_cache_kvq_amd import calib
+from quantized_kv_cache_kvq_amd.cache import LayerCache, PlaneSpec as GSpec
+import synth
+
+ATOL = 2e-3
+U32 = 2.0 ** -24
+
+
+def specs(wl, layer=0, kcodec=None, vcodec=None):
+    """(gpu K spec, gpu V spec, oracle K spec, oracle V spec) of a workload."""
+    kc = kcodec or wl.kcodec
+    vc = vcodec or wl.vcodec
+    if wl.basis == "plain":
+        return GSpec(kc), GSpec(vc), OSpec(kc), OSpec(vc)
+    if wl.basis == "hadamard":
+        wk = synth.kvarn_normalizers(wl, layer, "k")
+        wv = synth.kvarn_normalizers(wl, layer, "v")
+        return (GSpec(kc, "hadamard", w=wk), GSpec(vc, "hadamard", w=wv),
+                OSpec(kc, "hadamard", w=wk.numpy()), OSpec(vc, "hadamard", w=wv.numpy()))
+    ranks = [r for r, _ in wl.lowrank[: wl.Hkv]]
+    hcod = ["q%d_1" % b for _, b in wl.lowrank[: wl.Hkv]]
+    bases = [synth.basis(wl, layer, h).numpy() for h in range(wl.Hkv)]
+    P_or = [oracle.cobra.projection(U, r) for U, r in zip(bases, ranks)]
+    P_dev = calib.lowrank_projections(bases, ranks)
+    for h, r in enumerate(ranks):
+        assert np.array_equal(P_dev[h, :, :r].numpy(), P_or[h]), "projection builders disagree"
+    g = GSpec("", "lowrank", proj=P_dev, ranks=ranks, head_codecs=hcod)
+    o = OSpec("", "lowrank", P=P_or, head_codec=hcod)
+    return g, g, o, o
+
+
+def new_cache(wl, capacity, gk, gv, device, N=None):
+    N = wl.N if N is None else N
+    return LayerCache(wl.B, wl.Hkv, capacity, N, gk, gv, device)
+
+
+def upload(cache, name, packed, tail_bytes=None):
+    b = cache.bufs[name]
+    b["codes"][: packed["codes"].size].copy_(torch.from_numpy(packed["codes"]))
+    for key in ("scales", "mins"):
+        if packed.get(key) is not None:
+            b[key].copy_(torch.from_numpy(packed[key].view(np.uint8)))
+    if tail_bytes is not None and b["tail"] is not None:
+        b["tail"].copy_(torch.from_numpy(tail_bytes))
+
+
+def download(cache, name):
+    b = cache.bufs[name]
+    out = {"codes": b["codes"].cpu().numpy()}
+    for key in ("scales", "mins"):
+        out[key] = b[key].cpu().numpy().view(np.uint16) if b[key] is not None else None
+    out["tail"] = b["tail"].cpu().numpy() if b["tail"] is not None else None
+    return out
+
+
+def oracle_layer_bytes(x, ospec, capacity, N):
+    enc = OL.encode_plane(x, ospec)
+    packed = OL.pack_plane(enc, ospec, capacity)
+    tail = OL.pack_tail(OL.tail_ring(x, N)) if N > 0 else None
+    return enc, packed, tail
+
+
+# ------------------------------------------------- tie-tolerant comparison --
+
+def _coord_error_bound(x, spec, h):
+    """Bound on |device - exact| of the stored coordinates of raw rows x."""
+    x = np.asarray(x, np.float64)
+    if spec.basis == "hadamard":
+        z = np.abs(x * spec.w[h].astype(np.float64))
+        return 9 * U32 * z.sum(-1, keepdims=True) * np.ones_like(x)
+    P = np.abs(spec.P[h].astype(np.float64))
+    return (D_LOWRANK_TERMS + 2) * U32 * (np.abs(x) @ P)
+
+
+D_LOWRANK_TERMS = 128
+
+
+def _f16_neighbours(v):
+    v16 = np.float16(v)
+    return {float(v16), float(np.nextafter(v16, np.float16(np.inf))),
+            float(np.nextafter(v16, np.float16(-np.inf)))}
+
+
+def check_rotated_head(x, enc_gpu, spec, h, max_frac=1e-3):
+    """Compare device encodings of raw rows x [T,128] of head h against the
+    oracle under the tie rule.  Returns (n_mismatch, n_codes)."""
+    codec = spec.codec_of(h)
+    fam, b = CODECS[codec]
+    L = spec.block_len(h)
+    y = OL.stored_coords(x, spec, h)                        # exact, fp64
+    err = _coord_error_bound(x, spec, h)
+    T, n = y.shape
+    yb = y.reshape(T, n // L, L)
+    eb = err.reshape(T, n // L, L)
+    cg = enc_gpu["codes"].reshape(T, n // L, L)
+    dg = enc_gpu["scales"].astype(np.float64)
+    ref = OL.encode_head(x, spec, h)
+    cr = ref["codes"].reshape(T, n // L, L)
+    dr = ref["scales"].astype(np.float64)
+    bad_scale = np.argwhere(dg != dr)
+    for (t, j) in bad_scale:
+        blk, e = yb[t, j], eb[t, j].max()
+        if fam == "0":
+            qm = 2 ** (b - 1) - 1
+            amax = np.abs(blk).max()
+            ok = dg[t, j] in _f16_neighbours(amax / qm) and abs(
+                np.float16((amax + e) / qm) - np.float16((amax - e) / qm)) > 0
+        else:
+            ok = True   # _1 scale/min move together; codes re-checked below with device values
+        assert ok, "scale of block (%d,%d) differs off a rounding midpoint" % (t, j)
+    if fam == "1":
+        mg = enc_gpu["mins"].astype(np.float64)
+        mr = ref["mins"].astype(np.float64)
+        for (t, j) in np.argwhere(mg != mr):
+            e = eb[t, j].max()
+            lo = yb[t, j].min()
+            assert np.float16(lo + e) != np.float16(lo - e), "min differs off a midpoint"
+    # codes against the device's own scale (and min)
+    d = dg[..., None]
+    if fam == "0":
+        qm = 2 ** (b - 1) - 1
+        quot = np.where(d == 0, 0.0, yb / np.where(d == 0, 1, d))
+        lo_c, hi_c = -qm, qm
+    else:
+        m = enc_gpu["mins"].astype(np.float64)[..., None]
+        quot = np.where(d == 0, 0.0, (yb - m) / np.where(d == 0, 1, d))
+        lo_c, hi_c = 0, 2 ** b - 1
+    tol = np.where(d == 0, 0.0, eb / np.where(d == 0, 1, d)) + 1e-4
+    expect = np.clip(np.rint(quot), lo_c, hi_c)
+    diff = cg != expect
+    ok_tie = (np.abs(cg - expect) <= 1) & (
+        (np.abs(quot - cg) <= 0.5 + tol) | ((cg == lo_c) & (quot < lo_c)) | ((cg == hi_c) & (quot > hi_c)))
+    assert np.all(ok_tie | ~diff), "codes off by more than a tie"
+    # count against the oracle's own codes as well
+    n_mis = int(np.sum(cg != cr))
+    assert n_mis <= max_frac * cg.size + 0, (n_mis, cg.size)
+    return n_mis, cg.size
+
+
+def unpack(cache, name, ospec, T):
+    buf = download(cache, name)
+    return OL.unpack_plane(buf, ospec, cache.batch, cache.n_kv_heads, cache.capacity, T), buf
