@@ -164,7 +164,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int MAX_BODY_SPLITS = 1024;
 constexpr int MAX_TAIL_SPLITS = 64;
-constexpr int TAIL_TT = 128;
+constexpr int TAIL_TT = 64;
+constexpr int TAIL_TILES_PER_SPLIT = 4;
 
 int max_splits(const kvq_layer &L) {
   const int tt = decode_tile_tokens(L.k.codec, L.v.codec, L.k.basis);
@@ -331,8 +332,11 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
   if (body_tiles > 0) {
     int want = body_splits;
     if (want == 0) {
+      // two 4-wave workgroups per CU, at least 4 tiles (one per wave) each
       const int target = 2 * device_cus();
       want = (target + units - 1) / units;
+      const int by_tiles = (body_tiles + 3) / 4;
+      if (want > by_tiles) want = by_tiles;
     }
     if (want > MAX_BODY_SPLITS) want = MAX_BODY_SPLITS;
     if (want > body_tiles) want = body_tiles;
@@ -345,7 +349,8 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
   }
   const int tail_tiles = (P.tail_tokens + TAIL_TT - 1) / TAIL_TT;
   if (tail_tiles > 0) {
-    int want = tail_tiles < MAX_TAIL_SPLITS ? tail_tiles : MAX_TAIL_SPLITS;
+    int want = (tail_tiles + TAIL_TILES_PER_SPLIT - 1) / TAIL_TILES_PER_SPLIT;
+    if (want > MAX_TAIL_SPLITS) want = MAX_TAIL_SPLITS;
     P.tiles_per_split_tail = (tail_tiles + want - 1) / want;
     P.S_tail = (tail_tiles + P.tiles_per_split_tail - 1) / P.tiles_per_split_tail;
   } else {

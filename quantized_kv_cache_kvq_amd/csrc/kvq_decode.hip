@@ -124,37 +124,80 @@ __global__ __launch_bounds__(64) void lowrank_query_kernel(const float *__restri
 
 // ---------------------------------------------------------------- combine --
 
-// One wave per (batch entry, query head); lane l owns output channels 2l, 2l+1.
-__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, float *__restrict__ out) {
+// One 256-thread workgroup per (batch entry, query head).  Split weights
+// 2^(m_s - M) are computed once (thread per split), the outputs are summed
+// by 4 split-groups x 64 channel pairs, then one wave takes the body sum
+// back to the raw basis and writes the normalised result.
+constexpr int CMB_MAX_SPLITS = 1024 + 64;
+
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, float *__restrict__ out) {
+  __shared__ float wts[CMB_MAX_SPLITS];
+  __shared__ float red[4][2][D];
+  __shared__ float sred[2][8];
+  __shared__ float olow[D];
   const int bh = blockIdx.x;
   const int h = bh % a.Hq;
   const int g = h / a.G;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *pr = a.part + (long long)bh * a.S_total * PSTRIDE;
 
-  const int nv = a.v.basis == KVQ_BASIS_LOWRANK ? a.v.hrank[g] : D;
-  float Mb = NEG_INF, Mt = NEG_INF;
-  for (int s = 0; s < a.S_body; ++s) Mb = fmaxf(Mb, pr[s * PSTRIDE]);
-  for (int s = a.S_body; s < a.S_total; ++s) Mt = fmaxf(Mt, pr[s * PSTRIDE]);
+  // segment maxima (body: splits [0, S_body), tail: [S_body, S_total))
+  float mb = NEG_INF, mt = NEG_INF;
+  for (int s = tid; s < a.S_total; s += 256) {
+    const float m = pr[(long long)s * PSTRIDE];
+    if (s < a.S_body) mb = fmaxf(mb, m); else mt = fmaxf(mt, m);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+  }
+  if (lane == 0) { sred[0][wave] = mb; sred[1][wave] = mt; }
+  __syncthreads();
+  const float Mb = fmaxf(fmaxf(sred[0][0], sred[0][1]), fmaxf(sred[0][2], sred[0][3]));
+  const float Mt = fmaxf(fmaxf(sred[1][0], sred[1][1]), fmaxf(sred[1][2], sred[1][3]));
+  __syncthreads();
 
-  float Lb = 0.f, Lt = 0.f;
+  // split weights and segment sums of l
+  float lb = 0.f, lt = 0.f;
+  for (int s = tid; s < a.S_total; s += 256) {
+    const float *p = pr + (long long)s * PSTRIDE;
+    const float Mseg = s < a.S_body ? Mb : Mt;
+    const float w = p[0] == NEG_INF ? 0.f : exp2f(p[0] - Mseg);
+    wts[s] = w;
+    if (s < a.S_body) lb = fmaf(w, p[1], lb); else lt = fmaf(w, p[1], lt);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lb += __shfl_xor(lb, o, 64);
+    lt += __shfl_xor(lt, o, 64);
+  }
+  if (lane == 0) { sred[0][4 + wave] = lb; sred[1][4 + wave] = lt; }
+  __syncthreads();
+  const float Lb = sred[0][4] + sred[0][5] + sred[0][6] + sred[0][7];
+  const float Lt = sred[1][4] + sred[1][5] + sred[1][6] + sred[1][7];
+
+  // weighted sums of the partial outputs: wave w takes splits w, w + 4, ...
   float ob0 = 0.f, ob1 = 0.f, ot0 = 0.f, ot1 = 0.f;
-  for (int s = 0; s < a.S_body; ++s) {
-    const float *p = pr + s * PSTRIDE;
-    const float wgt = p[0] == NEG_INF ? 0.f : exp2f(p[0] - Mb);
-    Lb = fmaf(wgt, p[1], Lb);
-    if (2 * lane < nv) ob0 = fmaf(wgt, p[4 + 2 * lane], ob0);
-    if (2 * lane + 1 < nv) ob1 = fmaf(wgt, p[5 + 2 * lane], ob1);
+  for (int s = wave; s < a.S_total; s += 4) {
+    const float2 v = *reinterpret_cast<const float2 *>(pr + (long long)s * PSTRIDE + 4 + 2 * lane);
+    const float w = wts[s];
+    if (s < a.S_body) { ob0 = fmaf(w, v.x, ob0); ob1 = fmaf(w, v.y, ob1); }
+    else { ot0 = fmaf(w, v.x, ot0); ot1 = fmaf(w, v.y, ot1); }
   }
-  for (int s = a.S_body; s < a.S_total; ++s) {
-    const float *p = pr + s * PSTRIDE;
-    const float wgt = p[0] == NEG_INF ? 0.f : exp2f(p[0] - Mt);
-    Lt = fmaf(wgt, p[1], Lt);
-    ot0 = fmaf(wgt, p[4 + 2 * lane], ot0);
-    ot1 = fmaf(wgt, p[5 + 2 * lane], ot1);
-  }
+  red[wave][0][2 * lane] = ob0;
+  red[wave][0][2 * lane + 1] = ob1;
+  red[wave][1][2 * lane] = ot0;
+  red[wave][1][2 * lane + 1] = ot1;
+  __syncthreads();
+  if (wave != 0) return;
+  ob0 = red[0][0][2 * lane] + red[1][0][2 * lane] + red[2][0][2 * lane] + red[3][0][2 * lane];
+  ob1 = red[0][0][2 * lane + 1] + red[1][0][2 * lane + 1] + red[2][0][2 * lane + 1] + red[3][0][2 * lane + 1];
+  ot0 = red[0][1][2 * lane] + red[1][1][2 * lane] + red[2][1][2 * lane] + red[3][1][2 * lane];
+  ot1 = red[0][1][2 * lane + 1] + red[1][1][2 * lane + 1] + red[2][1][2 * lane + 1] + red[3][1][2 * lane + 1];
 
   // body partial back to the raw basis
+  const int nv = a.v.basis == KVQ_BASIS_LOWRANK ? a.v.hrank[g] : D;
   if (a.S_body > 0) {
     if (a.v.basis == KVQ_BASIS_HADAMARD) {
       float x0 = ob0, x1 = ob1;
@@ -172,10 +215,11 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, float *__rest
       ob0 = x0 * (1.f / 128.f) / w[2 * lane];
       ob1 = x1 * (1.f / 128.f) / w[2 * lane + 1];
     } else if (a.v.basis == KVQ_BASIS_LOWRANK) {
-      __shared__ float olow[D];
-      olow[2 * lane] = ob0;
-      olow[2 * lane + 1] = ob1;
-      __syncthreads();
+      olow[2 * lane] = 2 * lane < nv ? ob0 : 0.f;
+      olow[2 * lane + 1] = 2 * lane + 1 < nv ? ob1 : 0.f;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const uint16_t *P = a.v.proj + (long long)g * D * D;
       float y0 = 0.f, y1 = 0.f;
       for (int k = 0; k < nv; ++k) {
@@ -200,8 +244,8 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, float *__rest
 // --------------------------------------------------------------- launcher --
 
 int decode_tile_tokens(int kcodec, int vcodec, int basis) {
-  if (basis == KVQ_BASIS_LOWRANK) return 256;
-  return tile_tokens_for(kcodec, vcodec);
+  (void)kcodec; (void)vcodec; (void)basis;
+  return 64;   // one wave tile; a split owns whole multiples of it
 }
 
 int decode_head_group(int G) {
@@ -211,11 +255,11 @@ int decode_head_group(int G) {
   return 1;
 }
 
-extern template hipError_t launch_decode_hg<1>(const DecodeArgs &, dim3, hipStream_t);
-extern template hipError_t launch_decode_hg<2>(const DecodeArgs &, dim3, hipStream_t);
-extern template hipError_t launch_decode_hg<4>(const DecodeArgs &, dim3, hipStream_t);
-extern template hipError_t launch_decode_hg<6>(const DecodeArgs &, dim3, hipStream_t);
-extern template hipError_t launch_decode_hg<8>(const DecodeArgs &, dim3, hipStream_t);
+extern template hipError_t launch_decode_hg<1>(const DecodeArgs &, hipStream_t);
+extern template hipError_t launch_decode_hg<2>(const DecodeArgs &, hipStream_t);
+extern template hipError_t launch_decode_hg<4>(const DecodeArgs &, hipStream_t);
+extern template hipError_t launch_decode_hg<6>(const DecodeArgs &, hipStream_t);
+extern template hipError_t launch_decode_hg<8>(const DecodeArgs &, hipStream_t);
 
 bool decode_lowrank_supported(int codec, int rank) { return decode_lowrank_supported_impl(codec, rank); }
 
@@ -255,20 +299,19 @@ hipError_t launch_decode(const DecodeArgs &args, const float *q, float sm_scale,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const dim3 grid((unsigned)((long long)a.B * a.Hkv * a.NHG * a.S_total));
   hipError_t r;
   switch (a.HG) {
-    case 1: r = launch_decode_hg<1>(a, grid, stream); break;
-    case 2: r = launch_decode_hg<2>(a, grid, stream); break;
-    case 4: r = launch_decode_hg<4>(a, grid, stream); break;
-    case 6: r = launch_decode_hg<6>(a, grid, stream); break;
-    case 8: r = launch_decode_hg<8>(a, grid, stream); break;
+    case 1: r = launch_decode_hg<1>(a, stream); break;
+    case 2: r = launch_decode_hg<2>(a, stream); break;
+    case 4: r = launch_decode_hg<4>(a, stream); break;
+    case 6: r = launch_decode_hg<6>(a, stream); break;
+    case 8: r = launch_decode_hg<8>(a, stream); break;
     default: r = hipErrorNotSupported;
   }
   if (r != hipSuccess) return r;
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(64), 0, stream, a, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(256), 0, stream, a, out);
   return hipGetLastError();
 }
 

@@ -49,6 +49,6 @@ bool decode_lowrank_supported(int codec, int rank);
 bool decode_pair_supported(int kcodec, int vcodec, int hg);
 
 template <int HG>
-hipError_t launch_decode_hg(const DecodeArgs &a, dim3 grid, hipStream_t st);
+hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st);
 
 }  // namespace kvq
