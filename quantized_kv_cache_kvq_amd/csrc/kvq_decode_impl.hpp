@@ -111,23 +111,74 @@ struct Cfg {
   static constexpr int VBITS = codec_bits(VC), VFAM = codec_family(VC);
   static constexpr int RK = row_bytes(KC, NK), CK = chunk_bytes(RK);
   static constexpr int RV = row_bytes(VC, NV), CV = chunk_bytes(RV);
-  static constexpr int NKB = NK < 32 ? 1 : NK / 32;          // 32-channel MFMA k-blocks
+  static constexpr int NKB = NK < 32 ? 1 : NK / 32;          // 32-channel QK k-blocks
   static constexpr int NBK = KFAM == FAM_F16 ? 0 : NK / block_len(NK);
   static constexpr int LV = VFAM == FAM_F16 ? NV : block_len(NV);
-  static constexpr int NBV = VFAM == FAM_F16 ? 1 : NV / LV;
-  static constexpr int NGRP = (HG + 3) / 4;                  // 16-lane row groups with heads
-  static constexpr int HGP = (HG + 3) / 4 * 4;
-  static constexpr int PITCH = ((RV + 15) / 16) * 16 + 16;   // LDS row pitch of V
-  static constexpr int NGV = NV / 8;                         // 8-channel groups of PV
-  static constexpr int NSLOT = 64 / NGV;
-  // LDS per wave: V rows, p*d weights, per-head query scalars
-  static constexpr int W_V = 64 * PITCH;
-  static constexpr int W_PD = 64 * NBV * HGP * 4;
-  static constexpr int W_Q = 8 * 4 + 8 * 4 * 4;              // inverse scales, block sums
-  static constexpr int W_BYTES = (W_V + W_PD + W_Q + 15) / 16 * 16;
+  static constexpr int NBV = VFAM == FAM_F16 ? 1 : NV / LV;  // value scale blocks
+  static constexpr int NDT = NV / 16;                        // 16-channel output tiles
+  static constexpr int TT = (KFAM == FAM_F16 || VFAM == FAM_F16) ? 32 : 64;  // wave tile
+  static constexpr int NT = TT / 16;                         // QK N-tiles per tile
+  static constexpr int NCH = TT / 32;                        // PV K-chunks per tile
+  static constexpr int TPT = 64 / TT;                        // lanes per token (staging)
+  static constexpr int NGQ = (HG + 1) / 2;                   // row groups holding heads
+  // LDS per wave: value rows (byte codes or binary16), weights [j][t][16
+  // rows] binary16, probabilities [h][t] fp32, per-head query scalars
+  static constexpr int VPITCH = VFAM == FAM_F16 ? 2 * NV + 32 : NV + 16;
+  static constexpr int W_V = TT * VPITCH;
+  static constexpr int W_A = NBV * TT * 32;
+  static constexpr int W_P = 8 * TT * 4;
+  static constexpr int W_Q = 8 * 4 + 8 * 4 * 4;
+  static constexpr int W_BYTES = (W_V + W_A + W_P + W_Q + 15) / 16 * 16;
   static constexpr int MERGE = NWAVE * HG * (NV + 4) * 4;
   static constexpr int LDS_BYTES = cmax<NWAVE * W_BYTES, MERGE>::value;
+  static_assert(2 * HG <= 16, "at most 8 query heads per workgroup");
+  static_assert(TT == 64 || VFAM == FAM_F16 || (RV / 2) % CV == 0,
+                "half-row staging needs chunk-aligned halves");
 };
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+
+// 8 binary16 values of MFMA operand rows from a token-major LDS array via
+// the gfx950 transposing load (4 x 16-bit per read, two reads).
+__device__ __forceinline__ half8 tr16_pair(const uint8_t *p0, const uint8_t *p1) {
+  typedef __attribute__((address_space(3))) short4v lds_s4;
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p0));
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p1));
+  H8 o;
+  o.u[0] = (uint32_t)(uint16_t)a.x | ((uint32_t)(uint16_t)a.y << 16);
+  o.u[1] = (uint32_t)(uint16_t)a.z | ((uint32_t)(uint16_t)a.w << 16);
+  o.u[2] = (uint32_t)(uint16_t)b.x | ((uint32_t)(uint16_t)b.y << 16);
+  o.u[3] = (uint32_t)(uint16_t)b.z | ((uint32_t)(uint16_t)b.w << 16);
+  return o.h;
+}
+
+// 8 byte codes (offset binary u) via the 8-bit transposing load.
+__device__ __forceinline__ uint2 tr8(const uint8_t *p) {
+  typedef __attribute__((address_space(3))) int2v lds_i2;
+  const int2v v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2 *)(p));
+  return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+
+// Offset-binary byte codes u -> exact binary16 (u - off).
+__device__ __forceinline__ half8 bytes_to_half8(uint2 x, float off) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const uint32_t c64 = 0x64646464u;
+  H8 o;
+  o.u[0] = __builtin_amdgcn_perm(c64, x.x, 0x04010400u);
+  o.u[1] = __builtin_amdgcn_perm(c64, x.x, 0x04030402u);
+  o.u[2] = __builtin_amdgcn_perm(c64, x.y, 0x04010400u);
+  o.u[3] = __builtin_amdgcn_perm(c64, x.y, 0x04030402u);
+  const _Float16 bias = (_Float16)(-(1024.f + off));
+  const half2v bias2 = {bias, bias};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    half2v v = __builtin_bit_cast(half2v, o.u[p]);
+    v = v + bias2;
+    o.u[p] = __builtin_bit_cast(uint32_t, v);
+  }
+  return o.h;
+}
 
 // ------------------------------------------------ QK operand preparation --
 
@@ -250,25 +301,45 @@ struct SplitIO {
   long long part_head_stride;  // floats between consecutive heads' partials
 };
 
+__device__ __forceinline__ uint2 side_raw(const uint16_t *base, long long t, bool valid, int nb) {
+  if (!valid) return make_uint2(0u, 0u);
+  const uint16_t *p = base + t * nb;
+  if (nb == 4) return *reinterpret_cast<const uint2 *>(p);
+  if (nb == 2) return make_uint2(*reinterpret_cast<const uint32_t *>(p), 0u);
+  return make_uint2((uint32_t)*p, 0u);
+}
+
+__device__ __forceinline__ void unpack_side(uint2 r, float *v, int nb) {
+  v[0] = f16_bits_to_f32(r.x & 0xFFFF);
+  if (nb > 1) v[1] = f16_bits_to_f32(r.x >> 16);
+  if (nb > 2) { v[2] = f16_bits_to_f32(r.y & 0xFFFF); v[3] = f16_bits_to_f32(r.y >> 16); }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max16(x);
+  return fmaxf(fmaxf(read_lane(x, 0), read_lane(x, 16)), fmaxf(read_lane(x, 32), read_lane(x, 48)));
+}
+
 template <class C>
 __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
-  constexpr int HG = C::HG;
+  constexpr int HG = C::HG, TT = C::TT, NT = C::NT, NDT = C::NDT, NBV = C::NBV;
+  constexpr int NBA = C::VFAM == FAM_F16 ? 1 : NBV;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   uint8_t *wl = lds + wave * C::W_BYTES;
-  uint8_t *vlds = wl;
-  float *pdlds = reinterpret_cast<float *>(wl + C::W_V);
-  float *qinv = reinterpret_cast<float *>(wl + C::W_V + C::W_PD);   // [8]
-  float *qsum = qinv + 8;                                            // [8][4]
+  uint8_t *vlds = wl;                                               // [TT][VPITCH]
+  uint8_t *alds = wl + C::W_V;                                      // [NBV][TT][16] f16
+  float *plds = reinterpret_cast<float *>(wl + C::W_V + C::W_A);    // [8][TT]
+  float *qinv = plds + 8 * TT;                                      // [8]
+  float *qsum = qinv + 8;                                           // [8][4]
 
-  const int n = lane & 15, g = lane >> 4;   // QK layout: token column, row group
-  const int gi = lane % C::NGV, slot = lane / C::NGV;   // PV layout
-  const int jv_g = (gi * 8) / C::LV;
+  const int n = lane & 15, g = lane >> 4;   // MFMA layout: column n, row group g
+  const int tl = lane % TT, tp = lane / TT; // staging layout: token tl, row part tp
 
-  // ---- query operands: row i = lane % 16 is head i (< HG), k-group = lane / 16
-  half8 qa_hi[C::NKB], qa_lo[C::NKB];
+  // ---- query operand: row i = lane % 16 is (head i/2, part i%2 = hi/lo)
+  half8 qa[C::NKB];
   {
-    const int i = n, kg = g;
+    const int i = n, kg = g, h = i >> 1, prt = i & 1;
     float v[C::NKB][8];
     float amax = 0.f;
 #pragma unroll
@@ -276,8 +347,8 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
       const int e0 = 32 * j + 8 * kg;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bool ok = i < HG && e0 + e < C::NK;
-        v[j][e] = ok ? io.q[i * D + e0 + e] * io.scale : 0.f;
+        const bool ok = h < HG && e0 + e < C::NK;
+        v[j][e] = ok ? io.q[h * D + e0 + e] * io.scale : 0.f;
         amax = fmaxf(amax, fabsf(v[j][e]));
       }
     }
@@ -289,73 +360,60 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
     const float up = ldexpf(1.f, sh);
 #pragma unroll
     for (int j = 0; j < C::NKB; ++j) {
-      H8 hi, lo;
-      float s = 0.f;
+      H8 a;
+      float ssum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = v[j][e] * up;
-        const _Float16 h = (_Float16)x;
-        hi.h[e] = h;
-        lo.h[e] = (_Float16)(x - (float)h);
-        s += v[j][e];
+        const _Float16 hi = (_Float16)x;
+        a.h[e] = prt ? (_Float16)(x - (float)hi) : hi;
+        ssum += v[j][e];
       }
-      qa_hi[j] = hi.h;
-      qa_lo[j] = lo.h;
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      if (g == 0 && i < HG && C::KFAM == FAM_1) qsum[i * 4 + j] = s;
+      qa[j] = a.h;
+      ssum += __shfl_xor(ssum, 16, 64);
+      ssum += __shfl_xor(ssum, 32, 64);
+      if (C::KFAM == FAM_1 && kg == 0 && prt == 0 && h < HG) qsum[h * 4 + j] = ssum;
     }
-    if (g == 0 && i < HG) qinv[i] = ldexpf(1.f, -sh);
+    if (kg == 0 && prt == 0 && h < HG) qinv[h] = ldexpf(1.f, -sh);
   }
   wave_sync_lds();
 
-  // per-lane copies for the QK layout (heads 4g + r)
-  float inv_r[4], qs_r[4][C::NKB];
+  // result layout (QK and PV alike): row group g holds heads 2g (rows 4g,
+  // 4g+1: hi, lo) and 2g+1 (rows 4g+2, 4g+3)
+  float inv_k[2], qs_k[2][C::NKB];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * g + r;
-    inv_r[r] = h < HG ? qinv[h] : 0.f;
+  for (int k = 0; k < 2; ++k) {
+    const int h = 2 * g + k;
+    inv_k[k] = h < HG ? qinv[h] : 0.f;
 #pragma unroll
-    for (int j = 0; j < C::NKB; ++j) qs_r[r][j] = (C::KFAM == FAM_1 && h < HG) ? qsum[h * 4 + j] : 0.f;
+    for (int j = 0; j < C::NKB; ++j) qs_k[k][j] = (C::KFAM == FAM_1 && h < HG) ? qsum[h * 4 + j] : 0.f;
   }
 
-  float m_run[4], l_lane[4];
-  float acc[HG][8];
-  float pm[C::NBV][4];
+  float m_run[2] = {NEG_INF, NEG_INF}, l_lane[2] = {0.f, 0.f};
+  float pm[NBV][2];
+  float O[NDT][2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = NEG_INF;
-    l_lane[r] = 0.f;
+  for (int j = 0; j < NBV; ++j) pm[j][0] = pm[j][1] = 0.f;
 #pragma unroll
-    for (int j = 0; j < C::NBV; ++j) pm[j][r] = 0.f;
-  }
-#pragma unroll
-  for (int h = 0; h < HG; ++h)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[h][k] = 0.f;
+  for (int dt = 0; dt < NDT; ++dt) O[dt][0] = O[dt][1] = 0.f;
 
-  // this wave's tiles: t_begin + 64 * (wave + NWAVE * i)
-  const long long first = io.t_begin + 64LL * wave;
-  const long long stride = 64LL * NWAVE;
+  // this wave's tiles: t_begin + TT * (wave + NWAVE * i)
+  const long long first = io.t_begin + (long long)TT * wave;
+  const long long stride = (long long)TT * NWAVE;
 
   // One full tile of register prefetch: while tile i is computed, every
-  // load of tile i+1 is in flight (K operands and scales of its 4 N-tiles,
-  // the lane's V row and the V scales its p*d weights need).
-  KRaw<C> kr[4][C::NKB];
-  uint2 ksr[4], kmr[4], vsr[4], vmr[4];
+  // load of tile i+1 is in flight.
+  KRaw<C> kr[NT][C::NKB];
+  uint2 ksr[NT], kmr[NT], vmr[NT];
+  uint2 vst = make_uint2(0u, 0u);
+  constexpr int NVCH = C::RV / C::CV;            // chunks per value row
+  constexpr int PCH = NVCH / C::TPT;             // chunks per staged part
+  constexpr int PB = C::RV / C::TPT;             // bytes per staged part
+  constexpr int VW = (PB + 3) / 4;
+  uint32_t vw[VW];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) ksr[nt] = kmr[nt] = vsr[nt] = vmr[nt] = make_uint2(0u, 0u);
-  constexpr int NVCH = C::RV / C::CV;
-  constexpr int NVW = (C::RV + 3) / 4;
-  uint32_t vw[NVW];
+  for (int nt = 0; nt < NT; ++nt) ksr[nt] = kmr[nt] = vmr[nt] = make_uint2(0u, 0u);
 
-  auto side_raw = [&](const uint16_t *base, long long t, bool valid, int nb) -> uint2 {
-    if (!valid) return make_uint2(0u, 0u);
-    const uint16_t *p = base + t * nb;
-    if (nb == 4) return *reinterpret_cast<const uint2 *>(p);
-    if (nb == 2) return make_uint2(*reinterpret_cast<const uint32_t *>(p), 0u);
-    return make_uint2((uint32_t)*p, 0u);
-  };
   auto load_k_nt = [&](long long t0, int nt) {
     const long long t = t0 + 16 * nt + n;
     const bool valid = t < io.t_end;
@@ -365,58 +423,56 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
     if constexpr (C::KFAM == FAM_1) kmr[nt] = side_raw(io.kmn, t, valid, C::NBK);
   };
   auto load_v = [&](long long t0) {
-    const long long t = t0 + lane;
+    const long long t = t0 + tl;
     const bool valid = t < io.t_end;
 #pragma unroll
-    for (int k = 0; k < NVW; ++k) vw[k] = 0u;
+    for (int k = 0; k < VW; ++k) vw[k] = 0u;
     if (valid) {
 #pragma unroll
-      for (int k = 0; k < NVCH; ++k) {
+      for (int kk = 0; kk < PCH; ++kk) {
+        const int k = tp * PCH + kk;
         const uint8_t *p = io.vcodes + tiled_offset(t, k, C::RV, C::CV);
         if constexpr (C::CV == 16) {
           const uint4 v = *reinterpret_cast<const uint4 *>(p);
-          vw[4 * k] = v.x; vw[4 * k + 1] = v.y; vw[4 * k + 2] = v.z; vw[4 * k + 3] = v.w;
+          vw[4 * kk] = v.x; vw[4 * kk + 1] = v.y; vw[4 * kk + 2] = v.z; vw[4 * kk + 3] = v.w;
         } else if constexpr (C::CV == 8) {
           const uint2 v = *reinterpret_cast<const uint2 *>(p);
-          vw[2 * k] = v.x; vw[2 * k + 1] = v.y;
+          vw[2 * kk] = v.x; vw[2 * kk + 1] = v.y;
         } else if constexpr (C::CV == 4) {
-          vw[k] = *reinterpret_cast<const uint32_t *>(p);
+          vw[kk] = *reinterpret_cast<const uint32_t *>(p);
         } else if constexpr (C::CV == 2) {
-          vw[k / 2] |= (uint32_t)(*reinterpret_cast<const uint16_t *>(p)) << (16 * (k & 1));
+          vw[kk / 2] |= (uint32_t)(*reinterpret_cast<const uint16_t *>(p)) << (16 * (kk & 1));
         } else {
-          vw[k / 4] |= (uint32_t)(*p) << (8 * (k & 3));
+          vw[kk / 4] |= (uint32_t)(*p) << (8 * (kk & 3));
         }
       }
     }
-    if constexpr (C::VFAM != FAM_F16) {
+    if constexpr (C::VFAM != FAM_F16) vst = side_raw(io.vsc, t, valid, NBV);
+    if constexpr (C::VFAM == FAM_1) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const long long tv = t0 + 16 * nt + n;
-        const bool ok = tv < io.t_end;
-        vsr[nt] = side_raw(io.vsc, tv, ok, C::NBV);
-        if constexpr (C::VFAM == FAM_1) vmr[nt] = side_raw(io.vmn, tv, ok, C::NBV);
+        vmr[nt] = side_raw(io.vmn, tv, tv < io.t_end, NBV);
       }
     }
-  };
-  auto unpack_side = [&](uint2 r, float *v, int nb) {
-    v[0] = f16_bits_to_f32(r.x & 0xFFFF);
-    if (nb > 1) v[1] = f16_bits_to_f32(r.x >> 16);
-    if (nb > 2) { v[2] = f16_bits_to_f32(r.y & 0xFFFF); v[3] = f16_bits_to_f32(r.y >> 16); }
   };
 
   if (first < io.t_end) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) load_k_nt(first, nt);
+    for (int nt = 0; nt < NT; ++nt) load_k_nt(first, nt);
     load_v(first);
   }
+  for (int i = lane; i < C::W_A / 16; i += 64)
+    reinterpret_cast<uint4 *>(alds)[i] = make_uint4(0u, 0u, 0u, 0u);
 
   for (long long t0 = first; t0 < io.t_end; t0 += stride) {
     const long long tn = t0 + stride;
     const bool more = tn < io.t_end;
-    // ---- QK: 4 N-tiles of 16 tokens
-    float s[4][4];
+
+    // ---- QK on the matrix cores
+    float s[NT][2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       half8 kb[C::NKB];
 #pragma unroll
       for (int j = 0; j < C::NKB; ++j) kb[j] = k_convert<C>(kr[nt][j]);
@@ -424,185 +480,218 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
       if constexpr (C::KFAM != FAM_F16) unpack_side(ksr[nt], dk, C::NBK);
       if constexpr (C::KFAM == FAM_1) unpack_side(kmr[nt], mk, C::NBK);
       if (more) load_k_nt(tn, nt);      // registers of N-tile nt are free again
-
       const long long t = t0 + 16 * nt + n;
       const bool valid = t < io.t_end;
-      float sc[4] = {0.f, 0.f, 0.f, 0.f};
+      float a1[2] = {0.f, 0.f}, a2[2] = {0.f, 0.f};
       if constexpr (C::KFAM == FAM_F16) {
         floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < C::NKB; ++j) {
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[j], kb[j], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[j], kb[j], c, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = c[r] * inv_r[r];
+        for (int j = 0; j < C::NKB; ++j) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], kb[j], c, 0, 0, 0);
+        a1[0] = c[0] + c[1];
+        a1[1] = c[2] + c[3];
       } else {
 #pragma unroll
         for (int j = 0; j < C::NKB; ++j) {
-          floatx4 c = {0.f, 0.f, 0.f, 0.f};
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[j], kb[j], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[j], kb[j], c, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sc[r] = fmaf(dk[j], c[r] * inv_r[r], sc[r]);
-            if constexpr (C::KFAM == FAM_1) sc[r] = fmaf(mk[j], qs_r[r][j], sc[r]);
+          const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+          const floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], kb[j], z, 0, 0, 0);
+          a1[0] = fmaf(dk[j], c[0] + c[1], a1[0]);
+          a1[1] = fmaf(dk[j], c[2] + c[3], a1[1]);
+          if constexpr (C::KFAM == FAM_1) {
+            a2[0] = fmaf(mk[j], qs_k[0][j], a2[0]);
+            a2[1] = fmaf(mk[j], qs_k[1][j], a2[1]);
           }
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[nt][r] = (valid && 4 * g + r < HG) ? sc[r] : NEG_INF;
+      for (int k = 0; k < 2; ++k)
+        s[nt][k] = (valid && 2 * g + k < HG) ? fmaf(a1[k], inv_k[k], a2[k]) : NEG_INF;
     }
 
-    // ---- online softmax (per wave; heads 4g + r live in row group g)
-    float alpha[4], mnew[4];
+    // ---- online softmax (per wave)
+    float alpha[2], mnew[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mx = fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r]));
+    for (int k = 0; k < 2; ++k) {
+      float mx = s[0][k];
+#pragma unroll
+      for (int nt = 1; nt < NT; ++nt) mx = fmaxf(mx, s[nt][k]);
       mx = row_max16(mx);
-      mnew[r] = fmaxf(m_run[r], mx);
-      alpha[r] = (mnew[r] == NEG_INF) ? 1.f : exp2f(m_run[r] - mnew[r]);
-      m_run[r] = mnew[r];
+      mnew[k] = fmaxf(m_run[k], mx);
+      alpha[k] = (mnew[k] == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_run[k] - mnew[k]);
+      m_run[k] = mnew[k];
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mv[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (C::VFAM == FAM_1) unpack_side(vmr[nt], mv, NBV);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float p = __builtin_amdgcn_exp2f(s[nt][k] - mnew[k]);   // exp2(-inf) = 0
+        l_lane[k] = (nt == 0 ? l_lane[k] * alpha[k] : l_lane[k]) + p;
+        if (2 * g + k < HG) plds[(2 * g + k) * TT + 16 * nt + n] = p;
+        if constexpr (C::VFAM == FAM_1) {
+#pragma unroll
+          for (int j = 0; j < NBV; ++j) pm[j][k] = (nt == 0 ? pm[j][k] * alpha[k] : pm[j][k]) + p * mv[j];
+        }
+      }
     }
 
-    // ---- stage this tile's V row, then p * d_j weights
+    // ---- stage the value row part: offset-binary byte codes, or binary16
     {
-      uint8_t *row = vlds + lane * C::PITCH;
+      uint8_t *dst = vlds + tl * C::VPITCH;
+      if constexpr (C::VFAM == FAM_F16) {
+        dst += tp * PB;
 #pragma unroll
-      for (int k = 0; k < NVW; k += 4) {
-        if (k + 3 < NVW) {
-          *reinterpret_cast<uint4 *>(row + 4 * k) = make_uint4(vw[k], vw[k + 1], vw[k + 2], vw[k + 3]);
+        for (int k = 0; k < VW; k += 4)
+          *reinterpret_cast<uint4 *>(dst + 4 * k) = make_uint4(vw[k], vw[k + 1], vw[k + 2], vw[k + 3]);
+      } else if constexpr (C::VBITS == 8) {
+        dst += tp * (C::NV / C::TPT);
+        const uint32_t fl = C::VFAM == FAM_0 ? 0x80808080u : 0u;
+#pragma unroll
+        for (int k = 0; k < VW; k += 4)
+          *reinterpret_cast<uint4 *>(dst + 4 * k) = make_uint4(vw[k] ^ fl, vw[k + 1] ^ fl, vw[k + 2] ^ fl, vw[k + 3] ^ fl);
+      } else if constexpr (C::VBITS == 4) {
+        dst += tp * (C::NV / C::TPT);
+        const uint32_t fl = C::VFAM == FAM_0 ? 0x88888888u : 0u;
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+          const uint32_t x = vw[k] ^ fl;
+          const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+          *reinterpret_cast<uint2 *>(dst + 8 * k) =
+              make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+        }
+      } else {
+        constexpr int b = C::VBITS;
+        constexpr uint32_t off = C::VFAM == FAM_0 ? (1u << (b - 1)) : 0u;
+        constexpr uint32_t m = (1u << b) - 1u;
+        constexpr int NC = C::NV / C::TPT;       // codes in this part
+#pragma unroll
+        for (int c4 = 0; c4 < NC / 4; ++c4) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t u = ((uint32_t)field<b, false>(vw, (4 * c4 + e) * b) + off) & m;
+            w |= u << (8 * e);
+          }
+          *reinterpret_cast<uint32_t *>(dst + 4 * c4) = w;
+        }
+      }
+    }
+    const uint2 vst_cur = vst;
+    if (more) load_v(tn);               // value registers are free again
+    wave_sync_lds();                    // probabilities and rows visible
+
+    // ---- weights x = p * d_j * 2^(14 - e_j), split hi / lo, rows (head, part)
+    float back[NBA];
+    {
+      float dv[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (C::VFAM != FAM_F16) unpack_side(vst_cur, dv, NBV);
+      constexpr int H0 = 0, H1 = HG;       // heads this lane stages
+      float ps[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) ps[h] = (h < HG && (C::TPT == 1 || (h >> 2) == tp)) ? plds[h * TT + tl] : 0.f;
+      (void)H0; (void)H1;
+#pragma unroll
+      for (int j = 0; j < NBA; ++j) {
+        int ex = 1;
+        if constexpr (C::VFAM != FAM_F16) {
+          const float emax = wave_max(dv[j]);
+          ex = 0;
+          if (emax > 0.f) (void)frexpf(emax, &ex);
+        }
+        const float scl = ldexpf(dv[j], 14 - ex);
+        back[j] = ldexpf(1.f, ex - 14);
+        // rows (2h, 2h+1) = (hi, lo) of head h; rows >= 2*HG stay zero
+        uint32_t rw[HG];
+#pragma unroll
+        for (int h = 0; h < HG; ++h) {
+          const float x = ps[h] * scl;
+          const _Float16 hi = (_Float16)x;
+          const _Float16 lo = (_Float16)(x - (float)hi);
+          rw[h] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+        }
+        uint32_t *dst = reinterpret_cast<uint32_t *>(alds + ((j * TT) + tl) * 32);
+        if constexpr (C::TPT == 1) {
+          if constexpr (HG == 4) {
+            *reinterpret_cast<uint4 *>(dst) = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+          } else {
+#pragma unroll
+            for (int h = 0; h < HG; ++h) dst[h] = rw[h];
+          }
         } else {
 #pragma unroll
-          for (int kk = k; kk < NVW; ++kk) *reinterpret_cast<uint32_t *>(row + 4 * kk) = vw[kk];
+          for (int h = 0; h < HG; ++h)
+            if ((h >> 2) == tp) dst[h] = rw[h];
         }
       }
     }
-    uint2 vsc_cur[4], vmn_cur[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      vsc_cur[nt] = vsr[nt];
-      vmn_cur[nt] = vmr[nt];
-    }
-    if (more) load_v(tn);               // V registers are free again
+    wave_sync_lds();
 
+    // ---- PV on the matrix cores: A = weights [rows][32 tokens], B = values
+    floatx4 ct[NDT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const long long t = t0 + 16 * nt + n;
-      const bool valid = t < io.t_end;
-      float dvs[4] = {1.f, 1.f, 1.f, 1.f}, mvs[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (C::VFAM != FAM_F16) unpack_side(vsc_cur[nt], dvs, C::NBV);
-      if constexpr (C::VFAM == FAM_1) unpack_side(vmn_cur[nt], mvs, C::NBV);
-      float p[4];
+    for (int dt = 0; dt < NDT; ++dt) ct[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = (s[nt][r] == NEG_INF) ? 0.f : exp2f(s[nt][r] - mnew[r]);
-        l_lane[r] = (nt == 0 ? l_lane[r] * alpha[r] : l_lane[r]) + p[r];
-      }
-      if (g < C::NGRP) {
+    for (int kc = 0; kc < C::NCH; ++kc) {
+      const int tok = 32 * kc + 8 * g;
 #pragma unroll
-        for (int j = 0; j < C::NBV; ++j) {
-          float *dst = pdlds + ((16 * nt + n) * C::NBV + j) * C::HGP + 4 * g;
-          float4 wv;
-          wv.x = valid ? p[0] * dvs[j] : 0.f;
-          wv.y = valid ? p[1] * dvs[j] : 0.f;
-          wv.z = valid ? p[2] * dvs[j] : 0.f;
-          wv.w = valid ? p[3] * dvs[j] : 0.f;
-          *reinterpret_cast<float4 *>(dst) = wv;
-          if constexpr (C::VFAM == FAM_1) {
+      for (int j = 0; j < NBA; ++j) {
+        const uint8_t *pa = alds + ((j * TT) + tok + (n >> 2)) * 32 + 8 * (n & 3);
+        const half8 a = tr16_pair(pa, pa + 4 * 32);
+        constexpr int DPB = C::VFAM == FAM_F16 ? NDT : C::LV / 16;   // tiles per A operand
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              pm[j][r] = (nt == 0 ? pm[j][r] * alpha[r] : pm[j][r]) + (valid ? p[r] * mvs[j] : 0.f);
+        for (int d = 0; d < DPB; ++d) {
+          const int dt = j * DPB + d;
+          half8 bv;
+          if constexpr (C::VFAM == FAM_F16) {
+            const uint8_t *pb = vlds + (tok + (n >> 2)) * C::VPITCH + (16 * dt + 4 * (n & 3)) * 2;
+            bv = tr16_pair(pb, pb + 4 * C::VPITCH);
+          } else {
+            const uint8_t *pb = vlds + (tok + (n >> 1)) * C::VPITCH + 16 * dt + 8 * (n & 1);
+            constexpr float voff = C::VFAM == FAM_0 ? (float)(1 << (C::VBITS - 1)) : 0.f;
+            bv = bytes_to_half8(tr8(pb), voff);
           }
+          ct[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, ct[dt], 0, 0, 0);
         }
       }
     }
-
-    // accumulators of head h are rescaled by that head's alpha (from its row group)
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      const float a = read_lane(alpha[h & 3], 16 * (h >> 2));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[h][k] *= a;
+    for (int dt = 0; dt < NDT; ++dt) {
+      constexpr int DPB = C::VFAM == FAM_F16 ? NDT : C::LV / 16;
+      const float bk = back[dt / DPB];
+      O[dt][0] = fmaf(O[dt][0], alpha[0], (ct[dt][0] + ct[dt][1]) * bk);
+      O[dt][1] = fmaf(O[dt][1], alpha[1], (ct[dt][2] + ct[dt][3]) * bk);
     }
-    wave_sync_lds();
-
-    // ---- PV: channels 8*gi .. 8*gi+7 over tokens slot, slot + NSLOT, ...
-#pragma unroll 4
-    for (int u = slot; u < 64; u += C::NSLOT) {
-      const uint8_t *row = vlds + u * C::PITCH;
-      float val[8];
-      if constexpr (C::VFAM == FAM_F16) {
-        const uint4 rr = *reinterpret_cast<const uint4 *>(row + gi * 16);
-        const uint32_t ww[4] = {rr.x, rr.y, rr.z, rr.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          val[k] = f16_bits_to_f32((uint16_t)((ww[k >> 1] >> (16 * (k & 1))) & 0xFFFFu));
-      } else {
-        constexpr int VB = C::VBITS;
-        const int bit0 = gi * 8 * VB;
-        const uint32_t *rw = reinterpret_cast<const uint32_t *>(row);
-        const uint32_t lo = rw[bit0 >> 5];
-        const uint32_t hi = rw[(bit0 >> 5) + 1];
-        const int sh = bit0 & 31;
-        uint32_t a2[2];
-        a2[0] = sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
-        a2[1] = sh ? (hi >> sh) : hi;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) val[k] = (float)field<VB, C::VFAM == FAM_0>(a2, k * VB);
-      }
-      const float *pd = pdlds + (u * C::NBV + jv_g) * C::HGP;
-#pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        const float wgt = pd[h];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[h][k] = fmaf(wgt, val[k], acc[h][k]);
-      }
-    }
-    wave_sync_lds();
+    wave_sync_lds();                    // LDS tiles are free for the next tile
   }
 
-  // ---- close this wave: sums over the row's 16 lanes, accumulators over slots
-  float lsum[4], pmsum[C::NBV][4];
+  // ---- close this wave: l and pm over the row's 16 lanes
+  float lsum[2], pmsum[NBV][2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    lsum[r] = row_sum16(l_lane[r]);
+  for (int k = 0; k < 2; ++k) {
+    lsum[k] = row_sum16(l_lane[k]);
 #pragma unroll
-    for (int j = 0; j < C::NBV; ++j) pmsum[j][r] = C::VFAM == FAM_1 ? row_sum16(pm[j][r]) : 0.f;
+    for (int j = 0; j < NBV; ++j) pmsum[j][k] = C::VFAM == FAM_1 ? row_sum16(pm[j][k]) : 0.f;
   }
-#pragma unroll
-  for (int h = 0; h < HG; ++h)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float v = acc[h][k];
-#pragma unroll
-      for (int o = C::NGV; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      acc[h][k] = v;
-    }
   __syncthreads();   // every wave is done with its LDS tiles
 
   // merge area: [wave][h][4 + NV]: m, l, -, -, o[NV]
   float *mg = reinterpret_cast<float *>(lds);
   constexpr int MS = C::NV + 4;
 #pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    const int r = h & 3, grp = h >> 2;
-    float *dst = mg + (wave * HG + h) * MS;
-    if (lane == 16 * grp) {
-      dst[0] = m_run[r];
-      dst[1] = lsum[r];
-    }
-    float pmh = 0.f;   // min term of this lane's value block, head h
-    if constexpr (C::VFAM == FAM_1) {
-#pragma unroll
-      for (int j = 0; j < C::NBV; ++j) {
-        const float v = read_lane(pmsum[j][r], 16 * grp);
-        pmh = (j == jv_g) ? v : pmh;
+  for (int k = 0; k < 2; ++k) {
+    const int h = 2 * g + k;
+    if (h < HG) {
+      float *dst = mg + (wave * HG + h) * MS;
+      if (n == 0) {
+        dst[0] = m_run[k];
+        dst[1] = lsum[k];
       }
-    }
-    if (slot == 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) dst[4 + gi * 8 + k] = acc[h][k] + pmh;
+      for (int dt = 0; dt < NDT; ++dt) {
+        float o = O[dt][k];
+        if constexpr (C::VFAM == FAM_1) o += pmsum[(16 * dt) / C::LV][k];
+        dst[4 + 16 * dt + n] = o;
+      }
     }
   }
   __syncthreads();
@@ -630,15 +719,6 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
 
 // ------------------------------------------------------------- kernels ----
 
-__device__ inline void split_io_common(const DecodeArgs &a, int &b, int &kvh, int &hg, int &s) {
-  int id = blockIdx.x;
-  s = id % a.S_body;
-  id /= a.S_body;
-  hg = id % a.NHG;
-  id /= a.NHG;
-  kvh = id % a.Hkv;
-  b = id / a.Hkv;
-}
 
 template <class C>
 __device__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
@@ -681,35 +761,38 @@ __device__ void run_tail(const DecodeArgs &a, int b, int kvh, int hg, int s, uin
   attend_range<C>(io, lds);
 }
 
-// Occupancy targets (waves per SIMD) of the kernels: the register budget
-// is 512 / target per lane.
-template <int KC, int VC> struct Occ { static constexpr int value = (KC == KVQ_F16 || VC == KVQ_F16) ? 2 : 2; };
-
-// Plain / KVarN body splits with fixed codecs.
-template <int HG, int KC, int VC>
-__global__ __launch_bounds__(WG, (Occ<KC, VC>::value)) void decode_kernel(DecodeArgs a) {
-  using CB = Cfg<HG, KC, VC, D, D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[CB::LDS_BYTES];
-  int b, kvh, hg, s;
-  split_io_common(a, b, kvh, hg, s);
-  run_body<CB>(a, b, kvh, hg, s, lds);
+// Plain / KVarN body with fixed codecs, plus the binary16 tail splits in
+// the same launch (so the short tail work overlaps the body).  blockIdx
+// enumerates tail splits first, then body splits, of every (b, kv head,
+// head group).
+__device__ inline bool split_decode(const DecodeArgs &a, int &b, int &kvh, int &hg, int &s) {
+  const long long units = (long long)a.B * a.Hkv * a.NHG;
+  long long id = blockIdx.x;
+  bool tail = false;
+  if (id < units * a.S_tail) {
+    tail = true;
+    s = a.S_body + (int)(id % a.S_tail);
+    id /= a.S_tail;
+  } else {
+    id -= units * a.S_tail;
+    s = (int)(id % a.S_body);
+    id /= a.S_body;
+  }
+  hg = (int)(id % a.NHG);
+  id /= a.NHG;
+  kvh = (int)(id % a.Hkv);
+  b = (int)(id / a.Hkv);
+  return tail;
 }
 
-// Binary16 precision-tail splits (raw basis); blockIdx enumerates
-// (b, kv head, head group, tail split) and the partial lands at split
-// index S_body + tail split.
-template <int HG>
-__global__ __launch_bounds__(WG, 2) void decode_tail_kernel(DecodeArgs a) {
+template <int HG, int KC, int VC>
+__global__ __launch_bounds__(WG, 2) void decode_kernel(DecodeArgs a) {
+  using CB = Cfg<HG, KC, VC, D, D>;
   using CT = Cfg<HG, KVQ_F16, KVQ_F16, D, D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[CT::LDS_BYTES];
-  int id = blockIdx.x;
-  const int st = id % a.S_tail;
-  id /= a.S_tail;
-  const int hg = id % a.NHG;
-  id /= a.NHG;
-  const int kvh = id % a.Hkv;
-  const int b = id / a.Hkv;
-  run_tail<HG>(a, b, kvh, hg, a.S_body + st, lds);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[cmax<CB::LDS_BYTES, CT::LDS_BYTES>::value];
+  int b, kvh, hg, s;
+  if (split_decode(a, b, kvh, hg, s)) run_tail<HG>(a, b, kvh, hg, s, lds);
+  else run_body<CB>(a, b, kvh, hg, s, lds);
 }
 
 // Low-rank body: per-head (codec, rank) chosen at run time among the
@@ -722,15 +805,19 @@ __global__ __launch_bounds__(WG, 2) void decode_tail_kernel(DecodeArgs a) {
 
 template <int HG>
 struct LrLds {
-  static constexpr int bytes = cmax<Cfg<HG, KVQ_Q4_1, KVQ_Q4_1, 128, 128>::LDS_BYTES,
-                                    Cfg<HG, KVQ_Q3_1, KVQ_Q3_1, 128, 128>::LDS_BYTES>::value;
+  static constexpr int bytes = cmax<cmax<Cfg<HG, KVQ_Q4_1, KVQ_Q4_1, 128, 128>::LDS_BYTES,
+                                         Cfg<HG, KVQ_Q3_1, KVQ_Q3_1, 128, 128>::LDS_BYTES>::value,
+                                    Cfg<HG, KVQ_F16, KVQ_F16, D, D>::LDS_BYTES>::value;
 };
 
 template <int HG>
 __global__ __launch_bounds__(WG, 2) void decode_lowrank_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LrLds<HG>::bytes];
   int b, kvh, hg, s;
-  split_io_common(a, b, kvh, hg, s);
+  if (split_decode(a, b, kvh, hg, s)) {
+    run_tail<HG>(a, b, kvh, hg, s, lds);
+    return;
+  }
   const int codec = a.k.hcodec[kvh], rank = a.k.hrank[kvh];
 #define KVQ_LR_DISPATCH(CC, RR)                                                           \
   if (codec == CC && rank == RR) {                                                        \
@@ -760,13 +847,7 @@ inline bool decode_lowrank_supported_impl(int codec, int rank) {
 template <int HG>
 hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st) {
   const long long units = (long long)a.B * a.Hkv * a.NHG;
-  if (a.S_tail > 0) {
-    hipLaunchKernelGGL(decode_tail_kernel<HG>, dim3((unsigned)(units * a.S_tail)), dim3(WG), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.S_body == 0) return hipSuccess;
-  const dim3 grid((unsigned)(units * a.S_body));
+  const dim3 grid((unsigned)(units * (a.S_body + a.S_tail)));
   if (a.k.basis == KVQ_BASIS_LOWRANK) {
     hipLaunchKernelGGL(decode_lowrank_kernel<HG>, grid, dim3(WG), 0, st, a);
     return hipGetLastError();
