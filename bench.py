@@ -111,7 +111,7 @@ def setup(wl, dev, replicas):
     return reps, news, qs, codecs
 
 
-def cpu_baseline(wl, reps_layers, budget_s=20.0):
+def cpu_baseline(wl, reps_layers, budget_s=12.0):
     """The oracle (as it stands) decoding a bounded sample of the step on the
     host: whole (batch entry, kv head) units of layer 0, as many as fit the
     budget, on a thread pool of the host's cores (BLAS pinned to one thread
@@ -150,11 +150,12 @@ def cpu_baseline(wl, reps_layers, budget_s=20.0):
             Vt = OL.attention_kv(ve, vt, vspec, T, N)
             return attention.attend(q[b, h * G:(h + 1) * G], Kt[0], Vt[0], wl.sm_scale)
 
+    # whole passes over the units (at least one unit), until the budget
     t0 = time.perf_counter()
     done = 0
     with concurrent.futures.ThreadPoolExecutor(cores) as ex:
-        while done < len(units) and time.perf_counter() - t0 < budget_s:
-            batch = units[done: done + cores]
+        while time.perf_counter() - t0 < budget_s:
+            batch = [units[(done + i) % len(units)] for i in range(cores)]
             list(ex.map(unit, batch))
             done += len(batch)
     dt = time.perf_counter() - t0
@@ -162,10 +163,57 @@ def cpu_baseline(wl, reps_layers, budget_s=20.0):
     step_s = dt / frac
     nbytes = layer_bytes(wl, wl.kcodec, wl.vcodec, T)
     return {"value": nbytes / step_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d (batch entry, kv head) units of the step's decode (fp64 dequant + "
-                      "softmax attention over %d tokens), %.2f s wall, scaled to the full step"
-                      % (done, len(units), T, dt),
+            "sample": "%d (batch entry, kv head) decode units of layer 0 (the step has %d): fp64 "
+                      "dequantisation + softmax attention over %d tokens each, %.1f s wall on %d "
+                      "threads, scaled to the full step's bytes" % (done, len(units), T, dt, cores),
             "seconds_per_step": step_s}
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources and headers the kernels are built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_cache_kvq_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "kvq.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per split-K attention launch from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    factor), or None when that summary is missing, covers another workload,
+    or was taken on kernels whose sources have changed since."""
+    path = os.path.join(ROOT, "profiles", "decode_kernel_%s_traffic.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes, reps):
+    """A plain device-to-device copy of nbytes, reps times: the reference
+    kernel whose FETCH_SIZE / WRITE_SIZE calibrate the counter scale."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def main():
@@ -176,12 +224,17 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=synth.ORDER)
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe:
+        copy_probe(args.copy_probe, max(1, args.steps))
+        return
     lib.load()
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
@@ -205,16 +258,12 @@ def main():
                                          share_tail_with=s))
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
+    def step(i):
         layers = reps[i % len(reps)]
         for li, c in enumerate(layers):
             c.n_tokens = wl.T - 1
             c.append(news[li][0], news[li][1])
-            if ev is not None:
-                ev[0].record(stream)
             c.decode(qs[li], wl.sm_scale, out=outs[li])
-            if ev is not None:
-                ev[1].record(stream)
         if transcode_dst is not None:
             src, dst = transcode_dst
             layers[src].transcode_into(dst)
@@ -223,36 +272,41 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # whole steps
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    def timed(instrument):
+        if instrument:
+            lib.timing_begin(args.steps * len(codecs))
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / args.steps
+        return (ms,) + (lib.timing_end() if instrument else (0.0, 0))
 
-    # decode launches, bracketed one by one on the launch stream
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, pairs[i] if len(codecs) == 1 else None)
-    torch.cuda.synchronize()
-    if len(codecs) == 1:
-        dec_ms = sum(a.elapsed_time(b) for a, b in pairs) / args.steps
-        dec_bytes = step_bytes
-    else:
-        dec_ms, dec_bytes = None, None
+    # timed region: K whole steps.  Then the same K steps again with every
+    # split-K attention launch stamped by HIP events (hipExtLaunchKernel, on
+    # the stream it runs on) for the kernel's own average duration.
+    ms_per_step, _, _ = timed(False)
+    ms_instr, kern_ms, kern_n = timed(True)
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     ctx_tok_s = wl.B * wl.T * len(codecs) / (ms_per_step * 1e-3)
     roof = None
-    if dec_ms:
-        ach = dec_bytes / (dec_ms * 1e-3) / 1e9
+    if kern_n:
+        # algorithmic bytes per launch: the packed cache one layer's decode
+        # reads (codes, scales, mins, binary16 tail), averaged over layers
+        per_launch = step_bytes / len(codecs)
+        avg_ms = kern_ms / kern_n
+        ach = per_launch / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "decode attention (split kernel + combine)", "avg_launch_us": round(dec_ms * 1e3, 2)}
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(wl.name),
+                "kernel": "split-K decode attention (kvq::decode_kernel / decode_lowrank_kernel)",
+                "avg_launch_us": round(avg_ms * 1e3, 2), "launches": kern_n,
+                "ms_per_step_instrumented": round(ms_instr, 5),
+                "algorithmic_bytes_per_launch": per_launch}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, reps[0])

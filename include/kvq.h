@@ -174,6 +174,18 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q,
                                        void *ws, size_t ws_bytes, int32_t body_splits,
                                        void *stream);
 
+/* Measurement hook (not part of the cache format).  kvq_timing_begin
+ * creates 2*capacity host-side hipEvents on the current device; each later
+ * kvq_decode_attention* call records one pair on its stream, right before
+ * and after its split-K attention kernel (the kernel that reads the cache),
+ * until capacity pairs are used.  kvq_timing_end waits for the recorded
+ * events, returns the summed elapsed milliseconds and the number of pairs,
+ * destroys the events and stops recording (NULL outputs are allowed).  Not
+ * thread safe: one timing session per process.  capacity must be in
+ * [1, 1<<20]. */
+kvq_status kvq_timing_begin(int32_t capacity);
+kvq_status kvq_timing_end(double *total_ms, int32_t *count);
+
 const char *kvq_status_string(kvq_status status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *kvq_last_error(void);

@@ -401,4 +401,18 @@ kvq_status kvq_decode_attention(const kvq_layer *layer, const float *q, int32_t 
   return kvq_decode_attention_splits(layer, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream);
 }
 
+kvq_status kvq_timing_begin(int32_t capacity) {
+  if (capacity < 1 || capacity > (1 << 20))
+    return fail(KVQ_ERR_INVALID_ARG, "timing capacity %d outside [1, 1<<20]", capacity);
+  hipError_t e = kvq::timing_begin(capacity);
+  return e == hipSuccess ? ok() : hip_fail(e, "kvq_timing_begin");
+}
+
+kvq_status kvq_timing_end(double *total_ms, int32_t *count) {
+  int n = 0;
+  hipError_t e = kvq::timing_end(total_ms, &n);
+  if (count) *count = n;
+  return e == hipSuccess ? ok() : hip_fail(e, "kvq_timing_end");
+}
+
 }  // extern "C"

@@ -23,6 +23,7 @@
 // being computed (one tile of register prefetch).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include "kvq_common.hpp"
 #include "kvq_internal.hpp"
 
@@ -844,18 +845,20 @@ inline bool decode_lowrank_supported_impl(int codec, int rank) {
   X(KVQ_Q8_0, KVQ_Q2_0) X(KVQ_Q6_0, KVQ_Q4_0) X(KVQ_Q4_0, KVQ_Q2_0) X(KVQ_Q8_1, KVQ_Q4_1)  \
   X(KVQ_F16, KVQ_Q8_0) X(KVQ_F16, KVQ_Q4_0)
 
+// ev0/ev1 (may be null): events stamped with the split-K kernel's own start
+// and end (hipExtLaunchKernel), for timing without extra stream markers.
 template <int HG>
-hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st) {
+hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const long long units = (long long)a.B * a.Hkv * a.NHG;
   const dim3 grid((unsigned)(units * (a.S_body + a.S_tail)));
   if (a.k.basis == KVQ_BASIS_LOWRANK) {
-    hipLaunchKernelGGL(decode_lowrank_kernel<HG>, grid, dim3(WG), 0, st, a);
+    hipExtLaunchKernelGGL(decode_lowrank_kernel<HG>, grid, dim3(WG), 0, st, ev0, ev1, 0, a);
     return hipGetLastError();
   }
   const int kc = a.k.codec, vc = a.v.codec;
 #define KVQ_LAUNCH_PAIR(K, V)                                                               \
   if (kc == K && vc == V) {                                                                 \
-    hipLaunchKernelGGL((decode_kernel<HG, K, V>), grid, dim3(WG), 0, st, a);                \
+    hipExtLaunchKernelGGL((decode_kernel<HG, K, V>), grid, dim3(WG), 0, st, ev0, ev1, 0, a); \
     return hipGetLastError();                                                               \
   }
   KVQ_DECODE_PAIRS(KVQ_LAUNCH_PAIR)

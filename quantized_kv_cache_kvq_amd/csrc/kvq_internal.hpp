@@ -43,12 +43,20 @@ hipError_t launch_transcode(const PlaneArgs &src, const PlaneArgs &dst, int batc
 hipError_t launch_decode(const DecodeArgs &a, const float *q, float sm_scale, float *qw,
                          float *qsum, float *out, hipStream_t stream, bool prep, bool need_qsum);
 
+// Event timing of the split-K decode kernel (host side, not thread safe).
+hipError_t timing_begin(int capacity);
+hipError_t timing_end(double *total_ms, int *count);
+// Next free event pair (nulls when timing is off or the pool is used up);
+// timing_commit() marks it used once the launch went through.
+void timing_next(hipEvent_t *ev0, hipEvent_t *ev1);
+void timing_commit();
+
 int decode_tile_tokens(int kcodec, int vcodec, int basis);
 int decode_head_group(int G);
 bool decode_lowrank_supported(int codec, int rank);
 bool decode_pair_supported(int kcodec, int vcodec, int hg);
 
 template <int HG>
-hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace kvq

@@ -78,6 +78,8 @@ _SIGS = {
                                                    ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
                                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                                    ctypes.c_void_p]),
+    "kvq_timing_begin": (ctypes.c_int, [ctypes.c_int32]),
+    "kvq_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_abi_version": (ctypes.c_int32, []),
@@ -141,3 +143,15 @@ def decode_attention(layer, q_ptr, n_q_heads, sm_scale, out_ptr, ws_ptr, ws_byte
     check(load().kvq_decode_attention_splits(ctypes.byref(layer), q_ptr, n_q_heads,
                                              ctypes.c_float(sm_scale), out_ptr, ws_ptr, ws_bytes,
                                              body_splits, stream))
+
+
+def timing_begin(capacity):
+    """Start recording event pairs around the split-K decode kernel."""
+    check(load().kvq_timing_begin(capacity))
+
+
+def timing_end():
+    """(summed milliseconds, number of recorded launches); stops recording."""
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    check(load().kvq_timing_end(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

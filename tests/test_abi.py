@@ -101,7 +101,7 @@ def test_decode_validation(L):
     assert L.kvq_decode_attention(ctypes.byref(d), *bad) == lib.KVQ_ERR_INVALID_ARG    # 30 % 8
     need = lib.decode_workspace_bytes(d, 32)
     assert need > 0
-    small = (1, 32, ctypes.c_float(1.0), 1, 1, ctypes.c_size_t(need // 4), ctypes.c_void_p(0))
+    small = (1, 32, ctypes.c_float(1.0), 1, 1, ctypes.c_size_t(64), ctypes.c_void_p(0))
     assert L.kvq_decode_attention(ctypes.byref(d), *small) == lib.KVQ_ERR_WORKSPACE
     nows = (1, 32, ctypes.c_float(1.0), 1, None, ctypes.c_size_t(need), ctypes.c_void_p(0))
     assert L.kvq_decode_attention(ctypes.byref(d), *nows) == lib.KVQ_ERR_WORKSPACE
@@ -132,3 +132,13 @@ def test_lowrank_and_transcode_validation(L):
     b.k.codes = b.v.codes = 0x2000
     assert L.kvq_transcode_layer(ctypes.byref(a), ctypes.byref(b), None) == lib.KVQ_ERR_INVALID_ARG
     del e
+
+
+def test_timing_hook_host_side(L):
+    """The measurement hook rejects bad capacities before touching a device,
+    and ending a session that recorded nothing reports zero launches."""
+    assert L.kvq_timing_begin(0) == lib.KVQ_ERR_INVALID_ARG
+    assert L.kvq_timing_begin((1 << 20) + 1) == lib.KVQ_ERR_INVALID_ARG
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int32(-1)
+    assert L.kvq_timing_end(ctypes.byref(ms), ctypes.byref(n)) == lib.KVQ_OK
+    assert n.value == 0 and ms.value == 0.0
