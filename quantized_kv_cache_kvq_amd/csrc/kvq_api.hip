@@ -165,7 +165,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int MAX_BODY_SPLITS = 1024;
 constexpr int MAX_TAIL_SPLITS = 64;
 constexpr int TAIL_TT = 64;
-constexpr int TAIL_TILES_PER_SPLIT = 4;
+constexpr int TAIL_TILES_PER_SPLIT = DECODE_WG_WAVES;
 
 int max_splits(const kvq_layer &L) {
   const int tt = decode_tile_tokens(L.k.codec, L.v.codec, L.k.basis);
@@ -328,16 +328,42 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
   }
   P.tt_body = decode_tile_tokens(L.k.codec, L.v.codec, L.k.basis);
   const int units = P.B * P.Hkv * P.NHG;
+  const int tail_tiles = (P.tail_tokens + TAIL_TT - 1) / TAIL_TT;
   const int body_tiles = (P.body_tokens + P.tt_body - 1) / P.tt_body;
-  if (body_tiles > 0) {
-    int want = body_splits;
-    if (want == 0) {
-      // two 4-wave workgroups per CU, at least 4 tiles (one per wave) each
-      const int target = 2 * device_cus();
-      want = (target + units - 1) / units;
-      const int by_tiles = (body_tiles + 3) / 4;
-      if (want > by_tiles) want = by_tiles;
+  int tail_want = tail_tiles > 0 ? (tail_tiles + TAIL_TILES_PER_SPLIT - 1) / TAIL_TILES_PER_SPLIT : 0;
+  if (tail_want > MAX_TAIL_SPLITS) tail_want = MAX_TAIL_SPLITS;
+  int body_want = body_tiles > 0 ? 1 : 0;
+  if (body_tiles > 0 && body_splits > 0) {
+    body_want = body_splits;
+  } else if (body_tiles > 0) {
+    // One round of workgroups (the resident workgroups of all CUs hold the
+    // whole grid) with the same number of body tiles for every wave: tiles
+    // per split is a multiple of the waves per workgroup, the smallest that
+    // leaves a slot per unit for the tail; the tail takes the slots left.
+    const int per_unit = (DECODE_WG_PER_CU * device_cus()) / units;
+    const int need_tail = tail_tiles > 0 ? 1 : 0;
+    for (int tps = DECODE_WG_WAVES;; tps += DECODE_WG_WAVES) {
+      const int sb = (body_tiles + tps - 1) / tps;
+      if (sb + need_tail <= per_unit || sb == 1) {
+        body_want = sb;
+        if (tail_tiles > 0) {
+          int room = per_unit - sb;
+          if (room < 1) room = 1;
+          if (tail_want > room) tail_want = room;
+        }
+        break;
+      }
     }
+  }
+  if (tail_tiles > 0) {
+    P.tiles_per_split_tail = (tail_tiles + tail_want - 1) / tail_want;
+    P.S_tail = (tail_tiles + P.tiles_per_split_tail - 1) / P.tiles_per_split_tail;
+  } else {
+    P.tiles_per_split_tail = 1;
+    P.S_tail = 0;
+  }
+  if (body_tiles > 0) {
+    int want = body_want;
     if (want > MAX_BODY_SPLITS) want = MAX_BODY_SPLITS;
     if (want > body_tiles) want = body_tiles;
     if (want < 1) want = 1;
@@ -347,16 +373,6 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
     P.tiles_per_split_body = 1;
     P.S_body = 0;
   }
-  const int tail_tiles = (P.tail_tokens + TAIL_TT - 1) / TAIL_TT;
-  if (tail_tiles > 0) {
-    int want = (tail_tiles + TAIL_TILES_PER_SPLIT - 1) / TAIL_TILES_PER_SPLIT;
-    if (want > MAX_TAIL_SPLITS) want = MAX_TAIL_SPLITS;
-    P.tiles_per_split_tail = (tail_tiles + want - 1) / want;
-    P.S_tail = (tail_tiles + P.tiles_per_split_tail - 1) / P.tiles_per_split_tail;
-  } else {
-    P.tiles_per_split_tail = 1;
-    P.S_tail = 0;
-  }
   P.S_total = P.S_body + P.S_tail;
   P.prep = L.k.basis != KVQ_BASIS_PLAIN || codec_family(L.k.codec) == FAM_1;
   P.qsum = true;
@@ -365,8 +381,8 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
   if (!ws) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < W.total)
     return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, W.total);
-  if ((long long)units * P.S_total > 0x7fffffffLL)
-    return fail(KVQ_ERR_UNSUPPORTED, "grid too large");
+  if ((long long)P.Hkv * P.NHG > 65535 || P.B > 65535)
+    return fail(KVQ_ERR_UNSUPPORTED, "grid too large (kv heads x head groups or batch above 65535)");
 
   uint8_t *wsb = reinterpret_cast<uint8_t *>(ws);
   DecodeArgs a;

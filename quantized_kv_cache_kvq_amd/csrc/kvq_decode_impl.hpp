@@ -29,8 +29,8 @@
 
 namespace kvq {
 
-constexpr int WG = 256;
-constexpr int NWAVE = WG / 64;
+constexpr int NWAVE = DECODE_WG_WAVES;
+constexpr int WG = 64 * NWAVE;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 
@@ -470,6 +470,53 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
     const long long tn = t0 + stride;
     const bool more = tn < io.t_end;
 
+    // ---- stage the value row part: offset-binary byte codes, or binary16
+    {
+      uint8_t *dst = vlds + tl * C::VPITCH;
+      if constexpr (C::VFAM == FAM_F16) {
+        dst += tp * PB;
+#pragma unroll
+        for (int k = 0; k < VW; k += 4)
+          *reinterpret_cast<uint4 *>(dst + 4 * k) = make_uint4(vw[k], vw[k + 1], vw[k + 2], vw[k + 3]);
+      } else if constexpr (C::VBITS == 8) {
+        dst += tp * (C::NV / C::TPT);
+        const uint32_t fl = C::VFAM == FAM_0 ? 0x80808080u : 0u;
+#pragma unroll
+        for (int k = 0; k < VW; k += 4)
+          *reinterpret_cast<uint4 *>(dst + 4 * k) = make_uint4(vw[k] ^ fl, vw[k + 1] ^ fl, vw[k + 2] ^ fl, vw[k + 3] ^ fl);
+      } else if constexpr (C::VBITS == 4) {
+        dst += tp * (C::NV / C::TPT);
+        const uint32_t fl = C::VFAM == FAM_0 ? 0x88888888u : 0u;
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+          const uint32_t x = vw[k] ^ fl;
+          const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+          *reinterpret_cast<uint2 *>(dst + 8 * k) =
+              make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+        }
+      } else {
+        constexpr int b = C::VBITS;
+        constexpr uint32_t off = C::VFAM == FAM_0 ? (1u << (b - 1)) : 0u;
+        constexpr uint32_t m = (1u << b) - 1u;
+        constexpr int NC = C::NV / C::TPT;       // codes in this part
+#pragma unroll
+        for (int c4 = 0; c4 < NC / 4; ++c4) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t u = ((uint32_t)field<b, false>(vw, (4 * c4 + e) * b) + off) & m;
+            w |= u << (8 * e);
+          }
+          *reinterpret_cast<uint32_t *>(dst + 4 * c4) = w;
+        }
+      }
+    }
+    const uint2 vst_cur = vst;
+    uint2 vmr_cur[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) vmr_cur[nt] = vmr[nt];
+    if (more) load_v(tn);               // value registers are free: next tile's values load during this one
+
     // ---- QK on the matrix cores
     float s[NT][2];
 #pragma unroll
@@ -523,7 +570,7 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float mv[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (C::VFAM == FAM_1) unpack_side(vmr[nt], mv, NBV);
+      if constexpr (C::VFAM == FAM_1) unpack_side(vmr_cur[nt], mv, NBV);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const float p = __builtin_amdgcn_exp2f(s[nt][k] - mnew[k]);   // exp2(-inf) = 0
@@ -536,49 +583,6 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
       }
     }
 
-    // ---- stage the value row part: offset-binary byte codes, or binary16
-    {
-      uint8_t *dst = vlds + tl * C::VPITCH;
-      if constexpr (C::VFAM == FAM_F16) {
-        dst += tp * PB;
-#pragma unroll
-        for (int k = 0; k < VW; k += 4)
-          *reinterpret_cast<uint4 *>(dst + 4 * k) = make_uint4(vw[k], vw[k + 1], vw[k + 2], vw[k + 3]);
-      } else if constexpr (C::VBITS == 8) {
-        dst += tp * (C::NV / C::TPT);
-        const uint32_t fl = C::VFAM == FAM_0 ? 0x80808080u : 0u;
-#pragma unroll
-        for (int k = 0; k < VW; k += 4)
-          *reinterpret_cast<uint4 *>(dst + 4 * k) = make_uint4(vw[k] ^ fl, vw[k + 1] ^ fl, vw[k + 2] ^ fl, vw[k + 3] ^ fl);
-      } else if constexpr (C::VBITS == 4) {
-        dst += tp * (C::NV / C::TPT);
-        const uint32_t fl = C::VFAM == FAM_0 ? 0x88888888u : 0u;
-#pragma unroll
-        for (int k = 0; k < VW; ++k) {
-          const uint32_t x = vw[k] ^ fl;
-          const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-          *reinterpret_cast<uint2 *>(dst + 8 * k) =
-              make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
-        }
-      } else {
-        constexpr int b = C::VBITS;
-        constexpr uint32_t off = C::VFAM == FAM_0 ? (1u << (b - 1)) : 0u;
-        constexpr uint32_t m = (1u << b) - 1u;
-        constexpr int NC = C::NV / C::TPT;       // codes in this part
-#pragma unroll
-        for (int c4 = 0; c4 < NC / 4; ++c4) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t u = ((uint32_t)field<b, false>(vw, (4 * c4 + e) * b) + off) & m;
-            w |= u << (8 * e);
-          }
-          *reinterpret_cast<uint32_t *>(dst + 4 * c4) = w;
-        }
-      }
-    }
-    const uint2 vst_cur = vst;
-    if (more) load_v(tn);               // value registers are free again
     wave_sync_lds();                    // probabilities and rows visible
 
     // ---- weights x = p * d_j * 2^(14 - e_j), split hi / lo, rows (head, part)
@@ -718,6 +722,21 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
   }
 }
 
+#include "kvq_decode_q.hpp"
+
+// LDS of a body configuration: the integer-QK path for quantised K and V,
+// the binary16 path otherwise.
+template <class C, bool INT = (C::KFAM != FAM_F16 && C::VFAM != FAM_F16)>
+struct BodyLds {
+  static constexpr bool INT_QK = false;
+  static constexpr int bytes = C::LDS_BYTES;
+};
+template <class C>
+struct BodyLds<C, true> {
+  static constexpr bool INT_QK = true;
+  static constexpr int bytes = QCfg<C>::LDS_BYTES;
+};
+
 // ------------------------------------------------------------- kernels ----
 
 
@@ -739,7 +758,8 @@ __device__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uin
   io.t_end = io.t_begin + tps < a.body_tokens ? io.t_begin + tps : a.body_tokens;
   io.part = a.part + (((long long)b * a.Hq + head0) * a.S_total + s) * PSTRIDE;
   io.part_head_stride = (long long)a.S_total * PSTRIDE;
-  attend_range<C>(io, lds);
+  if constexpr (BodyLds<C>::INT_QK) attend_q<C>(io, lds);
+  else attend_range<C>(io, lds);
 }
 
 template <int HG>
@@ -763,34 +783,25 @@ __device__ void run_tail(const DecodeArgs &a, int b, int kvh, int hg, int s, uin
 }
 
 // Plain / KVarN body with fixed codecs, plus the binary16 tail splits in
-// the same launch (so the short tail work overlaps the body).  blockIdx
-// enumerates tail splits first, then body splits, of every (b, kv head,
-// head group).
+// the same launch (so the short tail work overlaps the body).  Grid:
+// x = split (tail splits first, then body splits), y = kv head * NHG +
+// head group, z = batch entry; one 32-bit division per workgroup.
 __device__ inline bool split_decode(const DecodeArgs &a, int &b, int &kvh, int &hg, int &s) {
-  const long long units = (long long)a.B * a.Hkv * a.NHG;
-  long long id = blockIdx.x;
-  bool tail = false;
-  if (id < units * a.S_tail) {
-    tail = true;
-    s = a.S_body + (int)(id % a.S_tail);
-    id /= a.S_tail;
-  } else {
-    id -= units * a.S_tail;
-    s = (int)(id % a.S_body);
-    id /= a.S_body;
-  }
-  hg = (int)(id % a.NHG);
-  id /= a.NHG;
-  kvh = (int)(id % a.Hkv);
-  b = (int)(id / a.Hkv);
+  const unsigned x = blockIdx.x, y = blockIdx.y;
+  const bool tail = x < (unsigned)a.S_tail;
+  s = tail ? a.S_body + (int)x : (int)x - a.S_tail;
+  const unsigned nhg = (unsigned)a.NHG;
+  kvh = (int)(y / nhg);
+  hg = (int)(y - (unsigned)kvh * nhg);
+  b = (int)blockIdx.z;
   return tail;
 }
 
 template <int HG, int KC, int VC>
-__global__ __launch_bounds__(WG, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs a) {
   using CB = Cfg<HG, KC, VC, D, D>;
   using CT = Cfg<HG, KVQ_F16, KVQ_F16, D, D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[cmax<CB::LDS_BYTES, CT::LDS_BYTES>::value];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[cmax<BodyLds<CB>::bytes, CT::LDS_BYTES>::value];
   int b, kvh, hg, s;
   if (split_decode(a, b, kvh, hg, s)) run_tail<HG>(a, b, kvh, hg, s, lds);
   else run_body<CB>(a, b, kvh, hg, s, lds);
@@ -806,13 +817,13 @@ __global__ __launch_bounds__(WG, 2) void decode_kernel(DecodeArgs a) {
 
 template <int HG>
 struct LrLds {
-  static constexpr int bytes = cmax<cmax<Cfg<HG, KVQ_Q4_1, KVQ_Q4_1, 128, 128>::LDS_BYTES,
-                                         Cfg<HG, KVQ_Q3_1, KVQ_Q3_1, 128, 128>::LDS_BYTES>::value,
+  static constexpr int bytes = cmax<cmax<BodyLds<Cfg<HG, KVQ_Q4_1, KVQ_Q4_1, 128, 128>>::bytes,
+                                         BodyLds<Cfg<HG, KVQ_Q3_1, KVQ_Q3_1, 128, 128>>::bytes>::value,
                                     Cfg<HG, KVQ_F16, KVQ_F16, D, D>::LDS_BYTES>::value;
 };
 
 template <int HG>
-__global__ __launch_bounds__(WG, 2) void decode_lowrank_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LrLds<HG>::bytes];
   int b, kvh, hg, s;
   if (split_decode(a, b, kvh, hg, s)) {
@@ -849,8 +860,7 @@ inline bool decode_lowrank_supported_impl(int codec, int rank) {
 // and end (hipExtLaunchKernel), for timing without extra stream markers.
 template <int HG>
 hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  const long long units = (long long)a.B * a.Hkv * a.NHG;
-  const dim3 grid((unsigned)(units * (a.S_body + a.S_tail)));
+  const dim3 grid((unsigned)(a.S_body + a.S_tail), (unsigned)(a.Hkv * a.NHG), (unsigned)a.B);
   if (a.k.basis == KVQ_BASIS_LOWRANK) {
     hipExtLaunchKernelGGL(decode_lowrank_kernel<HG>, grid, dim3(WG), 0, st, ev0, ev1, 0, a);
     return hipGetLastError();

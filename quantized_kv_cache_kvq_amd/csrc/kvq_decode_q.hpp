@@ -1,0 +1,547 @@
+// Quantised-body attention of one wave over its 64-token tiles, with the
+// QK product on the integer matrix cores.  Included by kvq_decode_impl.hpp
+// inside namespace kvq.
+//
+// QK (v_mfma_i32_16x16x32_i8).  The B operand is 16 tokens x 32 channels of
+// codes as bytes: 8-bit codes straight from memory, narrower codes expanded
+// in registers to offset-binary bytes.  The A operand holds the query as
+// exact integers: per head, q * 2^sh is rounded to an integer |qi| < 2^20
+// and written in three signed base-128 digits (one A row each), so every
+// product and sum is exact and the three partial results recombine as
+// c0 * 2^14 + c1 * 2^7 + c2.  Rows 4h + s = (head h, digit s); each 16-lane
+// row of the result then belongs to one head.  Block scales, code offsets
+// and _1 minima are applied to the integer block sums:
+//   s = 2^-sh * sum_j [ d_j (C_j + beta Q_j) + m_j Q_j ],  Q_j = sum of qi
+// over block j.  The query is rounded to ~21 significant bits relative to its
+// largest component (the binary32 input has 24).
+//
+// Softmax: online, per 16-lane row (= per head), in the log2 domain.
+//
+// PV (v_mfma_f32_16x16x32_f16): A = weights p * d_j (value block scale)
+// as binary16 hi + lo rows, staged in LDS by the lanes that computed p and
+// read back transposed; B = value codes staged as offset-binary bytes and
+// read with the transposing byte load.  Weights are scaled by 2^(28 - E_j),
+// E_j the largest binary16 exponent of block j's scales in the tile, so the
+// binary16 parts stay normal; the factor is undone on the fp32 result.
+#pragma once
+
+// Channel (0..7) held by byte e after expanding one 8-channel group of
+// B-bit codes to bytes.
+template <int B>
+__host__ __device__ constexpr int grp8_perm(int e) {
+  return B == 4 ? (e < 4 ? 2 * e : 2 * (e - 4) + 1)
+       : B == 2 ? (e < 4 ? (e == 0 ? 0 : e == 1 ? 4 : e == 2 ? 2 : 6)
+                         : (e == 4 ? 1 : e == 5 ? 5 : e == 6 ? 3 : 7))
+       : e;
+}
+
+// 8 codes of one group (LSB first in the low 8*B bits of w) as offset-binary
+// bytes u (u = c + 2^(B-1) for _0 codes, u = c for _1 codes); byte e holds
+// channel grp8_perm<B>(e).  8-bit codes are returned as stored.
+template <int B, int FAM>
+__device__ __forceinline__ uint2 group_bytes(uint64_t w) {
+  if constexpr (B == 8) {
+    return make_uint2((uint32_t)w, (uint32_t)(w >> 32));
+  } else if constexpr (B == 4) {
+    const uint32_t x = (uint32_t)w ^ (FAM == FAM_0 ? 0x88888888u : 0u);
+    return make_uint2(x & 0x0F0F0F0Fu, (x >> 4) & 0x0F0F0F0Fu);
+  } else if constexpr (B == 2) {
+    const uint32_t x = ((uint32_t)w & 0xFFFFu) ^ (FAM == FAM_0 ? 0xAAAAu : 0u);
+    const uint32_t e4 = x & 0x3333u, o4 = (x >> 2) & 0x3333u;   // codes 0,2,4,6 / 1,3,5,7
+    return make_uint2((e4 | (e4 << 12)) & 0x0F0F0F0Fu, (o4 | (o4 << 12)) & 0x0F0F0F0Fu);
+  } else if constexpr (B == 1) {
+    const uint32_t x = (uint32_t)w & 0xFFu;
+    return make_uint2(__umul24(x & 0xFu, 0x00204081u) & 0x01010101u,
+                      __umul24(x >> 4, 0x00204081u) & 0x01010101u);
+  } else {
+    constexpr uint64_t m = (1u << B) - 1u;
+    uint64_t sgn = 0;
+    if constexpr (FAM == FAM_0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sgn |= (uint64_t)1 << (B * i + B - 1);
+    }
+    const uint64_t x = w ^ sgn;
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i >> 2] |= (uint32_t)((x >> (B * i)) & m) << (8 * (i & 3));
+    return make_uint2(o[0], o[1]);
+  }
+}
+
+// Constants of the integer-QK path for a configuration.
+template <class C>
+struct QCfg {
+  static constexpr int HG = C::HG, NK = C::NK, NV = C::NV;
+  static constexpr int KB = C::KBITS, VB = C::VBITS;
+  static constexpr int TT = 64, NT = 4, NCH = 2;
+  static constexpr int HGRP = (HG + 3) / 4;            // 4-head row groups
+  static constexpr int NKB = NK < 32 ? 1 : NK / 32;    // 32-channel QK k-blocks
+  static constexpr int LK = block_len(NK);
+  static constexpr int NBK = NK / LK;                  // K scale blocks (== NKB)
+  static constexpr int LV = block_len(NV);
+  static constexpr int NBV = NV / LV;                  // V scale blocks
+  static constexpr int NDT = NV < 16 ? 1 : NV / 16;    // 16-channel PV tiles
+  static constexpr int DPB = LV / 16;                  // PV tiles per V block
+  static constexpr int RK = C::RK, CK = C::CK, RV = C::RV, CV = C::CV;
+  // stored code = byte + KBIAS (the K operand bytes)
+  static constexpr int KBIAS = C::KFAM == FAM_0 ? (KB == 8 ? 0 : -(1 << (KB - 1))) : (KB == 8 ? 128 : 0);
+  static constexpr float VOFF = C::VFAM == FAM_0 ? (float)(1 << (VB - 1)) : 0.f;
+  static constexpr int VPITCH = NV + 16;               // staged value row (bytes)
+  static constexpr int W_V = TT * VPITCH;
+  static constexpr int W_A = NBV * TT * 32;            // [j][t][16 rows] binary16
+  static constexpr int W_BYTES = (W_V + W_A + 15) / 16 * 16;
+  static constexpr int MERGE = NWAVE * HG * (NV + 4) * 4;
+  static constexpr int LDS_BYTES = cmax<NWAVE * W_BYTES, MERGE>::value;
+  static_assert(NKB == NBK, "QK k-blocks are scale blocks");
+  static_assert(KB == 1 || KB == 2 || KB == 4 || KB == 8 || KB == 3 || KB == 5 || KB == 6, "bits");
+};
+
+// Packed 16-bit unsigned max across the 16 lanes of a DPP row.
+__device__ __forceinline__ uint32_t row_max_u16x2(uint32_t x) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+#define KVQ_STEP(ctrl)                                                                          \
+  x = __builtin_bit_cast(uint32_t,                                                              \
+                         __builtin_elementwise_max(__builtin_bit_cast(us2, x),                  \
+                                                   __builtin_bit_cast(us2, (uint32_t)__builtin_amdgcn_update_dpp( \
+                                                       0, (int)x, ctrl, 0xF, 0xF, false))));
+  KVQ_STEP(0x128) KVQ_STEP(0x124) KVQ_STEP(0x122) KVQ_STEP(0x121)
+#undef KVQ_STEP
+  return x;
+}
+
+// Raw codes of the 8-channel group (k-block j, lane group g) of a token at
+// in-tile position tok: the low 8*B bits of the result.
+template <class Q>
+__device__ __forceinline__ uint64_t kq_load(const uint8_t *__restrict__ tile, int tok, int j, int g) {
+  constexpr int B = Q::KB, CK = Q::CK;
+  const int c0 = 32 * j + 8 * g;
+  if (c0 >= Q::NK) return 0;
+  const int b0 = c0 * B / 8;
+  if constexpr (B == 8 || B == 4 || B == 2 || B == 1) {
+    const uint8_t *p = tile + (unsigned)((b0 / CK) * (TILE * CK) + tok * CK + b0 % CK);
+    if constexpr (B == 8) {
+      const uint2 v = *reinterpret_cast<const uint2 *>(p);
+      return (uint64_t)v.x | ((uint64_t)v.y << 32);
+    } else if constexpr (B == 4) {
+      return *reinterpret_cast<const uint32_t *>(p);
+    } else if constexpr (B == 2) {
+      return *reinterpret_cast<const uint16_t *>(p);
+    } else {
+      return *p;
+    }
+  } else {
+    uint64_t w = 0;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int b = b0 + i;
+      w |= (uint64_t)tile[(unsigned)((b / CK) * (TILE * CK) + tok * CK + b % CK)] << (8 * i);
+    }
+    return w;
+  }
+}
+
+template <class C>
+__device__ void attend_q(const SplitIO &io, uint8_t *lds) {
+  using Q = QCfg<C>;
+  constexpr int HG = Q::HG, TT = Q::TT, NT = Q::NT, NKB = Q::NKB, NBV = Q::NBV, NDT = Q::NDT;
+  constexpr int HGRP = Q::HGRP, KB = Q::KB, VB = Q::VB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+  const int n = lane & 15, g = lane >> 4;
+  uint8_t *wl = lds + wave * Q::W_BYTES;
+  uint8_t *vlds = wl;                                              // [TT][VPITCH]
+  uint8_t *alds = wl + Q::W_V;                                     // [NBV][TT][16] f16
+
+  // the query rows this lane digitises (loaded before the tile loads so
+  // that waiting for them does not wait for the tile)
+  float qraw[HGRP][NKB][8];
+#pragma unroll
+  for (int rg = 0; rg < HGRP; ++rg) {
+    const int h = 4 * rg + (n >> 2);
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+      const int c0 = 32 * j + 8 * g;
+      if (h < HG && c0 < Q::NK) {
+        const float4 x0 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(h * D + c0));
+        const float4 x1 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(h * D + c0 + 4));
+        qraw[rg][j][0] = x0.x; qraw[rg][j][1] = x0.y; qraw[rg][j][2] = x0.z; qraw[rg][j][3] = x0.w;
+        qraw[rg][j][4] = x1.x; qraw[rg][j][5] = x1.y; qraw[rg][j][6] = x1.z; qraw[rg][j][7] = x1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qraw[rg][j][e] = 0.f;
+      }
+    }
+  }
+
+  // ---- tiles of this wave: t_begin + TT * (wave + NWAVE * i); 32-bit
+  // in-plane offsets; tokens past t_end load token t_end - 1 (masked later)
+  const int t_end = (int)io.t_end;
+  const int first = (int)io.t_begin + TT * wave;
+  constexpr int stride = TT * NWAVE;
+
+  uint64_t kr[NT][NKB];
+  uint2 ksr[NT], kmr[NT], vsr[NT], vmr[NT];
+  constexpr int VW = (Q::RV + 3) / 4;
+  uint32_t vw[VW];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) ksr[nt] = kmr[nt] = vsr[nt] = vmr[nt] = make_uint2(0u, 0u);
+
+  auto side = [&](const uint16_t *base, int t, int nb) -> uint2 {
+    const uint16_t *p = base + (unsigned)(t * nb);
+    if (nb == 4) return *reinterpret_cast<const uint2 *>(p);
+    if (nb == 2) return make_uint2(*reinterpret_cast<const uint32_t *>(p), 0u);
+    return make_uint2((uint32_t)*p, 0u);
+  };
+  auto load_k_nt = [&](int t0, int nt) {
+    const int tok = min(16 * nt + n, t_end - 1 - t0);
+    const uint8_t *tile = io.kcodes + (unsigned)t0 * Q::RK;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) kr[nt][j] = kq_load<Q>(tile, tok, j, g);
+    ksr[nt] = side(io.ksc, t0 + tok, Q::NBK);
+    if constexpr (C::KFAM == FAM_1) kmr[nt] = side(io.kmn, t0 + tok, Q::NBK);
+    vsr[nt] = side(io.vsc, t0 + tok, NBV);
+    if constexpr (C::VFAM == FAM_1) vmr[nt] = side(io.vmn, t0 + tok, NBV);
+  };
+  auto load_v = [&](int t0) {
+    const int tok = min(lane, t_end - 1 - t0);
+    const uint8_t *tile = io.vcodes + (unsigned)t0 * Q::RV;
+    constexpr int CV = Q::CV, NCV = Q::RV / CV;
+#pragma unroll
+    for (int k = 0; k < NCV; ++k) {
+      const uint8_t *p = tile + (unsigned)(k * (TILE * CV) + tok * CV);
+      if constexpr (CV == 16) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(p);
+        vw[4 * k] = x.x; vw[4 * k + 1] = x.y; vw[4 * k + 2] = x.z; vw[4 * k + 3] = x.w;
+      } else if constexpr (CV == 8) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(p);
+        vw[2 * k] = x.x; vw[2 * k + 1] = x.y;
+      } else if constexpr (CV == 4) {
+        vw[k] = *reinterpret_cast<const uint32_t *>(p);
+      } else if constexpr (CV == 2) {
+        const uint32_t x = *reinterpret_cast<const uint16_t *>(p);
+        if (k & 1) vw[k / 2] |= x << 16; else vw[k / 2] = x;
+      } else {
+        const uint32_t x = *p;
+        if (k & 3) vw[k / 4] |= x << (8 * (k & 3)); else vw[k / 4] = x;
+      }
+    }
+  };
+
+  // The first tile's loads go out before the query work below.  Loads are
+  // unconditional (a wave without tiles reads its split's first tile, and
+  // the last tile's prefetch re-reads the current tile, an L2 hit), so the
+  // compiler can count outstanding loads exactly and never has to drain
+  // the prefetched tile early.
+  {
+    const int lt0 = first < t_end ? first : (int)io.t_begin;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) load_k_nt(lt0, nt);
+    load_v(lt0);
+  }
+  __builtin_amdgcn_sched_barrier(0);    // keep the tile loads ahead of the query work
+
+  // ---- query digits: A row n of group rg = (head 4rg + n/4, digit n%4).
+  // Every lane also keeps 2^-sh and the block sums Q_j of head n/4; lane
+  // (n, g) of the QK result needs them for head g + 4rg (one shuffle each).
+  long qA[HGRP][NKB];
+  float inv[HGRP], Qb[HGRP][NKB], Qm[HGRP][NKB];
+#pragma unroll
+  for (int rg = 0; rg < HGRP; ++rg) {
+    const int h = 4 * rg + (n >> 2), dg = n & 3;
+    (void)h;
+    float v[NKB][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[j][e] = qraw[rg][j][grp8_perm<KB>(e)] * io.scale;
+        amax = fmaxf(amax, fabsf(v[j][e]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);
+    const int sh = 20 - ex;                         // |q * 2^sh| < 2^20
+    float qsj[NKB];
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+      uint32_t w[2] = {0u, 0u};
+      int qs = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int qi = (int)rintf(ldexpf(v[j][e], sh));
+        const int d2 = ((qi + 64) & 127) - 64;
+        const int r = (qi - d2) >> 7;
+        const int d1 = ((r + 64) & 127) - 64;
+        const int d0 = (r - d1) >> 7;
+        const int dig = (d0 & -(int)(dg == 0)) | (d1 & -(int)(dg == 1)) | (d2 & -(int)(dg == 2));
+        w[e >> 2] |= (uint32_t)(dig & 0xFF) << (8 * (e & 3));
+        qs += qi;
+      }
+      qA[rg][j] = (long)((uint64_t)w[0] | ((uint64_t)w[1] << 32));
+      qs += __shfl_xor(qs, 16, 64);
+      qs += __shfl_xor(qs, 32, 64);
+      qsj[j] = (float)qs;
+    }
+    // head g + 4rg lives in lanes 4g .. 4g+3 (any row group)
+    const bool live = g + 4 * rg < HG;
+    inv[rg] = live ? __shfl(ldexpf(1.f, -sh), 4 * g, 64) : 0.f;
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+      const float qs = live ? __shfl(qsj[j], 4 * g, 64) : 0.f;
+      Qb[rg][j] = (float)Q::KBIAS * qs;
+      Qm[rg][j] = qs;
+    }
+  }
+  for (int i = lane; i < Q::W_A / 16; i += 64)
+    reinterpret_cast<uint4 *>(alds)[i] = make_uint4(0u, 0u, 0u, 0u);
+
+  float m_run[HGRP], l_lane[HGRP], pm[HGRP][NBV], O[HGRP][NDT];
+#pragma unroll
+  for (int rg = 0; rg < HGRP; ++rg) {
+    m_run[rg] = NEG_INF;
+    l_lane[rg] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NBV; ++j) pm[rg][j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) O[rg][dt] = 0.f;
+  }
+
+  for (int t0 = first; t0 < t_end; t0 += stride) {
+    const int tn = t0 + stride < t_end ? t0 + stride : t0;   // prefetch target
+    const int lim = t_end - 1 - t0;
+
+    // ---- value row of token `lane` into LDS as offset-binary bytes; byte
+    // 8G + e holds channel 8G + grp8_perm<VB>(e)
+    {
+      uint8_t *dst = vlds + lane * Q::VPITCH;
+#pragma unroll
+      for (int G = 0; G < Q::NV / 8; ++G) {
+        uint64_t w;
+        if constexpr (VB == 8) {
+          w = (uint64_t)vw[2 * G] | ((uint64_t)vw[2 * G + 1] << 32);
+        } else if constexpr (VB == 4) {
+          w = vw[G];
+        } else if constexpr (VB == 2) {
+          w = (vw[G / 2] >> (16 * (G & 1))) & 0xFFFFu;
+        } else if constexpr (VB == 1) {
+          w = (vw[G / 4] >> (8 * (G & 3))) & 0xFFu;
+        } else {
+          // VB bytes starting at byte VB * G of the row
+          const int bit = 8 * VB * G;
+          const int wi = bit >> 5, sh = bit & 31;
+          uint64_t lo = (uint64_t)vw[wi] | ((wi + 1 < VW ? (uint64_t)vw[wi + 1] : 0) << 32);
+          if (sh + 8 * VB > 64 && wi + 2 < VW) lo = (lo >> sh) | ((uint64_t)vw[wi + 2] << (64 - sh));
+          else lo >>= sh;
+          w = lo;
+        }
+        uint2 b = group_bytes<VB, C::VFAM>(w);
+        if constexpr (VB == 8 && C::VFAM == FAM_0) { b.x ^= 0x80808080u; b.y ^= 0x80808080u; }
+        *reinterpret_cast<uint2 *>(dst + 8 * G) = b;
+      }
+    }
+    uint2 vs_cur[NT], vm_cur[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) { vs_cur[nt] = vsr[nt]; vm_cur[nt] = vmr[nt]; }
+    load_v(tn);
+
+    // ---- QK on the integer matrix cores
+    float sc[HGRP][NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float dk[4] = {1.f, 1.f, 1.f, 1.f}, mk[4] = {0.f, 0.f, 0.f, 0.f};
+      unpack_side(ksr[nt], dk, Q::NBK);
+      if constexpr (C::KFAM == FAM_1) unpack_side(kmr[nt], mk, Q::NBK);
+      long kb[NKB];
+#pragma unroll
+      for (int j = 0; j < NKB; ++j) {
+        const uint2 b = group_bytes<KB, C::KFAM>(kr[nt][j]);
+        uint2 bb = b;
+        if constexpr (KB == 8 && C::KFAM == FAM_1) { bb.x ^= 0x80808080u; bb.y ^= 0x80808080u; }
+        kb[j] = (long)((uint64_t)bb.x | ((uint64_t)bb.y << 32));
+      }
+      load_k_nt(tn, nt);                // N-tile nt's registers are free again
+      const bool valid = 16 * nt + n <= lim;
+#pragma unroll
+      for (int rg = 0; rg < HGRP; ++rg) {
+        float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NKB; ++j) {
+          typedef int intx4 __attribute__((ext_vector_type(4)));
+          const intx4 z = {0, 0, 0, 0};
+          const intx4 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(qA[rg][j], kb[j], z, 0, 0, 0);
+          float f = fmaf((float)c[0], 16384.f, (float)(c[1] * 128 + c[2]));
+          if constexpr (Q::KBIAS != 0) f += Qb[rg][j];
+          a1 = fmaf(dk[j], f, a1);
+          if constexpr (C::KFAM == FAM_1) a2 = fmaf(mk[j], Qm[rg][j], a2);
+        }
+        sc[rg][nt] = (valid && g + 4 * rg < HG) ? (a1 + a2) * inv[rg] : NEG_INF;
+      }
+    }
+
+    // ---- online softmax, one head per 16-lane row
+    float alpha[HGRP], p[HGRP][NT];
+#pragma unroll
+    for (int rg = 0; rg < HGRP; ++rg) {
+      float mx = sc[rg][0];
+#pragma unroll
+      for (int nt = 1; nt < NT; ++nt) mx = fmaxf(mx, sc[rg][nt]);
+      mx = row_max16(mx);
+      const float mnew = fmaxf(m_run[rg], mx);
+      alpha[rg] = m_run[rg] == NEG_INF ? (mnew == NEG_INF ? 1.f : 0.f) : __builtin_amdgcn_exp2f(m_run[rg] - mnew);
+      m_run[rg] = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        p[rg][nt] = mnew == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(sc[rg][nt] - mnew);
+        ps += p[rg][nt];
+      }
+      l_lane[rg] = fmaf(l_lane[rg], alpha[rg], ps);
+      if constexpr (C::VFAM == FAM_1) {
+#pragma unroll
+        for (int j = 0; j < NBV; ++j) {
+          float acc = pm[rg][j] * alpha[rg];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            float mv[4] = {0.f, 0.f, 0.f, 0.f};
+            unpack_side(vm_cur[nt], mv, NBV);
+            acc = fmaf(p[rg][nt], mv[j], acc);
+          }
+          pm[rg][j] = acc;
+        }
+      }
+    }
+
+    // ---- weights x = p * dv_j * 2^(28 - E_j) as (hi, lo) binary16 rows
+    // 4g + 2rg, 4g + 2rg + 1 of token 16nt + n
+    float back[NBV];
+    {
+      uint32_t e01 = 0u, e23 = 0u;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+        e01 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, e01),
+                  __builtin_bit_cast(us2, vs_cur[nt].x & 0x7C007C00u)));
+        if (NBV > 2)
+          e23 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, e23),
+                    __builtin_bit_cast(us2, vs_cur[nt].y & 0x7C007C00u)));
+      }
+      e01 = row_max_u16x2(e01);
+      if (NBV > 2) e23 = row_max_u16x2(e23);
+      float fwd[4];
+#pragma unroll
+      for (int j = 0; j < NBV; ++j) {
+        const uint32_t word = j < 2 ? e01 : e23;
+        int E = (int)((word >> (16 * (j & 1) + 10)) & 31u);
+        E = E < 1 ? 1 : E;
+        fwd[j] = __builtin_bit_cast(float, (uint32_t)(28 - E + 127) << 23);
+        back[j] = __builtin_bit_cast(float, (uint32_t)(E - 28 + 127) << 23);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float dv[4] = {1.f, 1.f, 1.f, 1.f};
+        unpack_side(vs_cur[nt], dv, NBV);
+#pragma unroll
+        for (int j = 0; j < NBV; ++j) {
+          const float scl = dv[j] * fwd[j];
+          uint32_t *dst = reinterpret_cast<uint32_t *>(alds + ((j * TT) + 16 * nt + n) * 32 + 8 * g);
+#pragma unroll
+          for (int rg = 0; rg < HGRP; ++rg) {
+            const float x = p[rg][nt] * scl;
+            const _Float16 hi = (_Float16)x;
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            dst[rg] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+          }
+        }
+      }
+    }
+    wave_sync_lds();
+
+    // ---- PV on the matrix cores: A = weights [16 rows][32 tokens], B = values
+    floatx4 ct[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) ct[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < Q::NCH; ++kc) {
+      const int tok = 32 * kc + 8 * g;
+#pragma unroll
+      for (int j = 0; j < NBV; ++j) {
+        const uint8_t *pa = alds + ((j * TT) + tok + (n >> 2)) * 32 + 8 * (n & 3);
+        const half8 a = tr16_pair(pa, pa + 4 * 32);
+#pragma unroll
+        for (int d = 0; d < Q::DPB; ++d) {
+          const int dt = j * Q::DPB + d;
+          const uint8_t *pb = vlds + (tok + (n >> 1)) * Q::VPITCH + 16 * dt + 8 * (n & 1);
+          const half8 bv = bytes_to_half8(tr8(pb), Q::VOFF);
+          ct[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, ct[dt], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const float bk = back[dt / Q::DPB];
+#pragma unroll
+      for (int rg = 0; rg < HGRP; ++rg)
+        O[rg][dt] = fmaf(O[rg][dt], alpha[rg], (ct[dt][2 * rg] + ct[dt][2 * rg + 1]) * bk);
+    }
+    wave_sync_lds();                    // LDS tiles are free for the next tile
+  }
+
+  // ---- close this wave: l and pm over the row's 16 lanes
+  float lsum[HGRP], pmsum[HGRP][NBV];
+#pragma unroll
+  for (int rg = 0; rg < HGRP; ++rg) {
+    lsum[rg] = row_sum16(l_lane[rg]);
+#pragma unroll
+    for (int j = 0; j < NBV; ++j) pmsum[rg][j] = C::VFAM == FAM_1 ? row_sum16(pm[rg][j]) : 0.f;
+  }
+  __syncthreads();   // every wave is done with its LDS tiles
+
+  // merge area: [wave][h][4 + NV]: m, l, -, -, o[NV] (raw channel order)
+  float *mg = reinterpret_cast<float *>(lds);
+  constexpr int MS = Q::NV + 4;
+#pragma unroll
+  for (int rg = 0; rg < HGRP; ++rg) {
+    const int h = g + 4 * rg;
+    if (h < HG) {
+      float *dst = mg + (wave * HG + h) * MS;
+      if (n == 0) {
+        dst[0] = m_run[rg];
+        dst[1] = lsum[rg];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int pos = 16 * dt + n;                       // staged byte position
+        if (pos < Q::NV) {
+          const int ch = 8 * (pos >> 3) + grp8_perm<VB>(pos & 7);
+          float o = O[rg][dt];
+          if constexpr (C::VFAM == FAM_1) o += pmsum[rg][pos / Q::LV];
+          dst[4 + ch] = o;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < HG * Q::NV; idx += WG) {
+    const int h = idx / Q::NV, c = idx % Q::NV;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mg[(w * HG + h) * MS]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      const float *src = mg + (w * HG + h) * MS;
+      const float wt = src[0] == NEG_INF ? 0.f : exp2f(src[0] - M);
+      o = fmaf(wt, src[4 + c], o);
+      L = fmaf(wt, src[1], L);
+    }
+    float *dst = io.part + h * io.part_head_stride;
+    dst[4 + c] = o;
+    if (c == 0) {
+      dst[0] = M;
+      dst[1] = L;
+    }
+  }
+}

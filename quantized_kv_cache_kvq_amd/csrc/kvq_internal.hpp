@@ -51,6 +51,11 @@ hipError_t timing_end(double *total_ms, int *count);
 void timing_next(hipEvent_t *ev0, hipEvent_t *ev1);
 void timing_commit();
 
+// Split-K decode workgroups: waves per workgroup and workgroups resident
+// per CU (the split policy sizes one round of workgroups from these).
+constexpr int DECODE_WG_WAVES = 8;
+constexpr int DECODE_WG_PER_CU = 1;
+
 int decode_tile_tokens(int kcodec, int vcodec, int basis);
 int decode_head_group(int G);
 bool decode_lowrank_supported(int codec, int rank);
