@@ -17,6 +17,24 @@
 
 namespace kvq {
 
+// All-reduce over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f<0x128>(x));
+  x = fmaxf(x, dpp_f<0x124>(x));
+  x = fmaxf(x, dpp_f<0x122>(x));
+  return fmaxf(x, dpp_f<0x121>(x));
+}
+__device__ __forceinline__ float row_min16(float x) {
+  x = fminf(x, dpp_f<0x128>(x));
+  x = fminf(x, dpp_f<0x124>(x));
+  x = fminf(x, dpp_f<0x122>(x));
+  return fminf(x, dpp_f<0x121>(x));
+}
+
 // In-wave fast Walsh-Hadamard transform of 128 values, lane l holding
 // elements 2l (a) and 2l+1 (b).  Butterflies (u+v, u-v) at every stride give
 // the Sylvester (natural-order) H applied to the vector.
@@ -110,6 +128,54 @@ __global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
   }
 
   const int bits = codec_bits(g.codec);
+  if (p.basis != KVQ_BASIS_LOWRANK && (bits == 8 || bits == 4 || bits == 2 || bits == 1)) {
+    // 128 coordinates, lane l holds 2l and 2l+1: block j is the DPP row of
+    // lanes 16j .. 16j+15, so block statistics are row reductions; the
+    // row's bits are gathered 16/bits lanes to a dword and stored whole.
+    const float a = coords[2 * lane], c = coords[2 * lane + 1];
+    const long long so = g.scales_off + (long long)t * 4 + (lane >> 4);
+    float d, m = 0.f;
+    if (fam == FAM_0) {
+      const float amax = row_max16(fmaxf(fabsf(a), fabsf(c)));
+      const float qmax = (float)((1 << (bits - 1)) - 1);
+      const uint16_t dh = f32_to_f16_bits(amax / qmax);
+      if ((lane & 15) == 0) p.scales[so] = dh;
+      d = f16_bits_to_f32(dh);
+    } else {
+      const float lo = row_min16(fminf(a, c)), hi = row_max16(fmaxf(a, c));
+      const uint16_t mh = f32_to_f16_bits(lo);
+      m = f16_bits_to_f32(mh);
+      const float R = hi - m;
+      const float levels = (float)((1 << bits) - 1);
+      const uint16_t dh = f32_to_f16_bits(R / levels);
+      if ((lane & 15) == 0) {
+        p.scales[so] = dh;
+        p.mins[so] = mh;
+      }
+      d = f16_bits_to_f32(dh);
+    }
+    const uint32_t mask = (1u << bits) - 1u;
+    uint32_t q0 = 0, q1 = 0;
+    if (d != 0.f) {
+      if (fam == FAM_0) {
+        const float qmax = (float)((1 << (bits - 1)) - 1);
+        q0 = (uint32_t)(int)fminf(fmaxf(rintf(a / d), -qmax), qmax);
+        q1 = (uint32_t)(int)fminf(fmaxf(rintf(c / d), -qmax), qmax);
+      } else {
+        const float levels = (float)((1 << bits) - 1);
+        q0 = (uint32_t)(int)fminf(fmaxf(rintf((a - m) / d), 0.f), levels);
+        q1 = (uint32_t)(int)fminf(fmaxf(rintf((c - m) / d), 0.f), levels);
+      }
+    }
+    const int K = 16 / bits;                       // lanes per dword
+    uint32_t w = ((q0 & mask) | ((q1 & mask) << bits)) << (2 * bits * (lane % K));
+    for (int o = 1; o < K; o <<= 1) w |= __shfl_xor(w, o, 64);
+    if (lane % K == 0) {
+      const int byte = 4 * (lane / K);
+      *reinterpret_cast<uint32_t *>(row_codes + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c) = w;
+    }
+    return;
+  }
   // 3. block scale (and min), one lane per block
   if (lane < g.nblk) {
     const float *blk = coords + lane * g.L;

@@ -126,121 +126,11 @@ __global__ __launch_bounds__(64) void lowrank_query_kernel(const float *__restri
 
 // ---------------------------------------------------------------- combine --
 
-// One 256-thread workgroup per (batch entry, query head).  Split weights
-// 2^(m_s - M) are computed once (thread per split), the outputs are summed
-// by 4 split-groups x 64 channel pairs, then one wave takes the body sum
-// back to the raw basis and writes the normalised result.
-constexpr int CMB_MAX_SPLITS = 1024 + 64;
-
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, float *__restrict__ out) {
-  __shared__ float wts[CMB_MAX_SPLITS];
-  __shared__ float red[4][2][D];
-  __shared__ float sred[2][8];
+// One wave per (batch entry, query head).
+__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, float *__restrict__ out) {
   __shared__ float olow[D];
   const int bh = blockIdx.x;
-  const int h = bh % a.Hq;
-  const int g = h / a.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float *pr = a.part + (long long)bh * a.S_total * PSTRIDE;
-
-  // segment maxima (body: splits [0, S_body), tail: [S_body, S_total))
-  float mb = NEG_INF, mt = NEG_INF;
-  for (int s = tid; s < a.S_total; s += 256) {
-    const float m = pr[(long long)s * PSTRIDE];
-    if (s < a.S_body) mb = fmaxf(mb, m); else mt = fmaxf(mt, m);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mb = fmaxf(mb, __shfl_xor(mb, o, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, o, 64));
-  }
-  if (lane == 0) { sred[0][wave] = mb; sred[1][wave] = mt; }
-  __syncthreads();
-  const float Mb = fmaxf(fmaxf(sred[0][0], sred[0][1]), fmaxf(sred[0][2], sred[0][3]));
-  const float Mt = fmaxf(fmaxf(sred[1][0], sred[1][1]), fmaxf(sred[1][2], sred[1][3]));
-  __syncthreads();
-
-  // split weights and segment sums of l
-  float lb = 0.f, lt = 0.f;
-  for (int s = tid; s < a.S_total; s += 256) {
-    const float *p = pr + (long long)s * PSTRIDE;
-    const float Mseg = s < a.S_body ? Mb : Mt;
-    const float w = p[0] == NEG_INF ? 0.f : exp2f(p[0] - Mseg);
-    wts[s] = w;
-    if (s < a.S_body) lb = fmaf(w, p[1], lb); else lt = fmaf(w, p[1], lt);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lb += __shfl_xor(lb, o, 64);
-    lt += __shfl_xor(lt, o, 64);
-  }
-  if (lane == 0) { sred[0][4 + wave] = lb; sred[1][4 + wave] = lt; }
-  __syncthreads();
-  const float Lb = sred[0][4] + sred[0][5] + sred[0][6] + sred[0][7];
-  const float Lt = sred[1][4] + sred[1][5] + sred[1][6] + sred[1][7];
-
-  // weighted sums of the partial outputs: wave w takes splits w, w + 4, ...
-  float ob0 = 0.f, ob1 = 0.f, ot0 = 0.f, ot1 = 0.f;
-  for (int s = wave; s < a.S_total; s += 4) {
-    const float2 v = *reinterpret_cast<const float2 *>(pr + (long long)s * PSTRIDE + 4 + 2 * lane);
-    const float w = wts[s];
-    if (s < a.S_body) { ob0 = fmaf(w, v.x, ob0); ob1 = fmaf(w, v.y, ob1); }
-    else { ot0 = fmaf(w, v.x, ot0); ot1 = fmaf(w, v.y, ot1); }
-  }
-  red[wave][0][2 * lane] = ob0;
-  red[wave][0][2 * lane + 1] = ob1;
-  red[wave][1][2 * lane] = ot0;
-  red[wave][1][2 * lane + 1] = ot1;
-  __syncthreads();
-  if (wave != 0) return;
-  ob0 = red[0][0][2 * lane] + red[1][0][2 * lane] + red[2][0][2 * lane] + red[3][0][2 * lane];
-  ob1 = red[0][0][2 * lane + 1] + red[1][0][2 * lane + 1] + red[2][0][2 * lane + 1] + red[3][0][2 * lane + 1];
-  ot0 = red[0][1][2 * lane] + red[1][1][2 * lane] + red[2][1][2 * lane] + red[3][1][2 * lane];
-  ot1 = red[0][1][2 * lane + 1] + red[1][1][2 * lane + 1] + red[2][1][2 * lane + 1] + red[3][1][2 * lane + 1];
-
-  // body partial back to the raw basis
-  const int nv = a.v.basis == KVQ_BASIS_LOWRANK ? a.v.hrank[g] : D;
-  if (a.S_body > 0) {
-    if (a.v.basis == KVQ_BASIS_HADAMARD) {
-      float x0 = ob0, x1 = ob1;
-      float s0 = x0 + x1, d0 = x0 - x1;
-      x0 = s0;
-      x1 = d0;
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        float p0 = __shfl_xor(x0, m, 64), p1 = __shfl_xor(x1, m, 64);
-        bool upper = (lane & m) != 0;
-        x0 = upper ? (p0 - x0) : (x0 + p0);
-        x1 = upper ? (p1 - x1) : (x1 + p1);
-      }
-      const float *w = a.v.w + (long long)g * D;
-      ob0 = x0 * (1.f / 128.f) / w[2 * lane];
-      ob1 = x1 * (1.f / 128.f) / w[2 * lane + 1];
-    } else if (a.v.basis == KVQ_BASIS_LOWRANK) {
-      olow[2 * lane] = 2 * lane < nv ? ob0 : 0.f;
-      olow[2 * lane + 1] = 2 * lane + 1 < nv ? ob1 : 0.f;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const uint16_t *P = a.v.proj + (long long)g * D * D;
-      float y0 = 0.f, y1 = 0.f;
-      for (int k = 0; k < nv; ++k) {
-        y0 = fmaf(f16_bits_to_f32(P[(long long)(2 * lane) * D + k]), olow[k], y0);
-        y1 = fmaf(f16_bits_to_f32(P[(long long)(2 * lane + 1) * D + k]), olow[k], y1);
-      }
-      ob0 = y0;
-      ob1 = y1;
-    }
-  }
-
-  const float M = fmaxf(Mb, Mt);
-  const float wb = Mb == NEG_INF ? 0.f : exp2f(Mb - M);
-  const float wt = Mt == NEG_INF ? 0.f : exp2f(Mt - M);
-  const float inv = 1.f / (wb * Lb + wt * Lt);
-  float2 o;
-  o.x = (wb * ob0 + wt * ot0) * inv;
-  o.y = (wb * ob1 + wt * ot1) * inv;
-  reinterpret_cast<float2 *>(out + (long long)bh * D)[lane] = o;
+  combine_head(a, out, bh / a.Hq, bh % a.Hq, olow);
 }
 
 // --------------------------------------------------------------- launcher --
@@ -377,7 +267,7 @@ hipError_t launch_decode(const DecodeArgs &args, const float *q, float sm_scale,
   if (ev0) timing_commit();
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(256), 0, stream, a, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(64), 0, stream, a, out);
   return hipGetLastError();
 }
 

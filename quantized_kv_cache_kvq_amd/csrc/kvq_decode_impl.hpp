@@ -782,6 +782,113 @@ __device__ void run_tail(const DecodeArgs &a, int b, int kvh, int hg, int s, uin
   attend_range<C>(io, lds);
 }
 
+// ------------------------------------------------------ split combine ----
+
+// Merge of one query head's split partials (the split-K decode of the
+// forum post: M = max m_s, L = sum l_s 2^(m_s - M), o = sum o_s 2^(m_s - M)
+// / L), one wave, in a single pass over the partials: every (m, l) and
+// output load is issued before any arithmetic waits on it.  Body partials
+// are in the stored basis and go back to the raw basis first (Hadamard
+// transform and 1/w for KVarN, P_h for low rank) before they meet the tail
+// partials.  `olow` holds 128 floats of LDS.
+__device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out, int b, int h,
+                                    float *olow) {
+  const int lane = threadIdx.x & 63;
+  const long long bh = (long long)b * a.Hq + h;
+  const float *pr = a.part + bh * a.S_total * PSTRIDE;
+  const int S = a.S_total, Sb = a.S_body;
+
+  // Two passes over the splits: segment maxima first (lane s reads m of
+  // split s), then weights, l sums and the weighted outputs, with 8 output
+  // loads in flight per step.
+  float mb = NEG_INF, mt = NEG_INF;
+  for (int s = lane; s < S; s += 64) {
+    const float m = pr[(long long)s * PSTRIDE];
+    if (s < Sb) mb = fmaxf(mb, m); else mt = fmaxf(mt, m);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+  }
+  float lb = 0.f, lt = 0.f, ob0 = 0.f, ob1 = 0.f, ot0 = 0.f, ot1 = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int s = s0 + lane;
+    float wgt = 0.f;
+    if (s < S) {
+      const float2 ml = *reinterpret_cast<const float2 *>(pr + (long long)s * PSTRIDE);
+      const float M = s < Sb ? mb : mt;
+      wgt = ml.x == NEG_INF ? 0.f : exp2f(ml.x - M);
+      if (s < Sb) lb = fmaf(wgt, ml.y, lb); else lt = fmaf(wgt, ml.y, lt);
+    }
+    const int cnt = S - s0 < 64 ? S - s0 : 64;
+    for (int i0 = 0; i0 < cnt; i0 += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k < cnt ? i0 + k : cnt - 1;
+        v[k] = *reinterpret_cast<const float2 *>(pr + (long long)(s0 + i) * PSTRIDE + 4 + 2 * lane);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k;
+        const float wi = i < cnt ? __shfl(wgt, i, 64) : 0.f;
+        if (s0 + i < Sb) {
+          ob0 = fmaf(wi, v[k].x, ob0);
+          ob1 = fmaf(wi, v[k].y, ob1);
+        } else {
+          ot0 = fmaf(wi, v[k].x, ot0);
+          ot1 = fmaf(wi, v[k].y, ot1);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lb += __shfl_xor(lb, o, 64);
+    lt += __shfl_xor(lt, o, 64);
+  }
+
+  // body sum back to the raw basis
+  const int g = h / a.G;
+  if (Sb > 0) {
+    if (a.v.basis == KVQ_BASIS_HADAMARD) {
+      float x0 = ob0 + ob1, x1 = ob0 - ob1;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(x0, m, 64), p1 = __shfl_xor(x1, m, 64);
+        const bool upper = (lane & m) != 0;
+        x0 = upper ? (p0 - x0) : (x0 + p0);
+        x1 = upper ? (p1 - x1) : (x1 + p1);
+      }
+      const float *wv = a.v.w + (long long)g * D;
+      ob0 = x0 * (1.f / 128.f) / wv[2 * lane];
+      ob1 = x1 * (1.f / 128.f) / wv[2 * lane + 1];
+    } else if (a.v.basis == KVQ_BASIS_LOWRANK) {
+      const int nv = a.v.hrank[g];
+      olow[2 * lane] = 2 * lane < nv ? ob0 : 0.f;
+      olow[2 * lane + 1] = 2 * lane + 1 < nv ? ob1 : 0.f;
+      wave_sync_lds();
+      const uint16_t *P = a.v.proj + (long long)g * D * D;
+      float y0 = 0.f, y1 = 0.f;
+      for (int k = 0; k < nv; ++k) {
+        y0 = fmaf(f16_bits_to_f32(P[(long long)(2 * lane) * D + k]), olow[k], y0);
+        y1 = fmaf(f16_bits_to_f32(P[(long long)(2 * lane + 1) * D + k]), olow[k], y1);
+      }
+      ob0 = y0;
+      ob1 = y1;
+    }
+  }
+  const float M = fmaxf(mb, mt);
+  const float wb = mb == NEG_INF ? 0.f : exp2f(mb - M);
+  const float wt = mt == NEG_INF ? 0.f : exp2f(mt - M);
+  const float inv = 1.f / (wb * lb + wt * lt);
+  float2 o;
+  o.x = (wb * ob0 + wt * ot0) * inv;
+  o.y = (wb * ob1 + wt * ot1) * inv;
+  reinterpret_cast<float2 *>(out + bh * D)[lane] = o;
+}
+
 // Plain / KVarN body with fixed codecs, plus the binary16 tail splits in
 // the same launch (so the short tail work overlaps the body).  Grid:
 // x = split (tail splits first, then body splits), y = kv head * NHG +
@@ -828,16 +935,13 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(De
   int b, kvh, hg, s;
   if (split_decode(a, b, kvh, hg, s)) {
     run_tail<HG>(a, b, kvh, hg, s, lds);
-    return;
-  }
-  const int codec = a.k.hcodec[kvh], rank = a.k.hrank[kvh];
+  } else {
+    const int codec = a.k.hcodec[kvh], rank = a.k.hrank[kvh];
 #define KVQ_LR_DISPATCH(CC, RR)                                                           \
-  if (codec == CC && rank == RR) {                                                        \
-    run_body<Cfg<HG, CC, CC, RR, RR>>(a, b, kvh, hg, s, lds);                             \
-    return;                                                                               \
-  }
-  KVQ_LR_CASES(KVQ_LR_DISPATCH)
+    if (codec == CC && rank == RR) run_body<Cfg<HG, CC, CC, RR, RR>>(a, b, kvh, hg, s, lds); else
+    KVQ_LR_CASES(KVQ_LR_DISPATCH) {}
 #undef KVQ_LR_DISPATCH
+  }
 }
 
 inline bool decode_lowrank_supported_impl(int codec, int rank) {
