@@ -152,16 +152,23 @@ kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const
 kvq_status kvq_transcode_layer(const kvq_layer *src, const kvq_layer *dst, void *stream);
 
 /* Workspace needed by kvq_decode_attention for this layer's shapes and
- * capacity (independent of n_tokens), in bytes. */
+ * capacity (independent of n_tokens), in bytes.  Its first 64 KiB hold
+ * split-completion counters: zero-fill a workspace once before its first
+ * use; every completed call leaves them zero again, and the rest of the
+ * workspace needs no initialisation. */
 size_t kvq_decode_workspace_bytes(const kvq_layer *layer, int32_t n_q_heads);
 
 /* Decode attention of one query per head over the first n_tokens tokens.
  * q: device binary32 [B][n_q_heads][128]; out: device binary32
  * [B][n_q_heads][128] (raw basis).  Scores are sm_scale * <q, k>.
- * n_q_heads must be a multiple of n_kv_heads; n_tokens >= 1.  ws: device
- * scratch of at least kvq_decode_workspace_bytes bytes (contents need no
- * initialisation and are clobbered).  Tokens t >= n_tokens - tail_len are
- * read from the tail. */
+ * n_q_heads must be a multiple of n_kv_heads; n_tokens >= 1 and
+ * batch * n_kv_heads * head groups <= 16384 (a head group is up to 8 query
+ * heads of one kv head).  ws: device scratch of at least
+ * kvq_decode_workspace_bytes bytes, zero-filled before its first use (see
+ * there); calls sharing a workspace must not overlap in time.  One kernel
+ * launch: the split that finishes its (batch, kv head, head group) last
+ * merges the splits into out.  Tokens t >= n_tokens - tail_len are read
+ * from the tail. */
 kvq_status kvq_decode_attention(const kvq_layer *layer, const float *q, int32_t n_q_heads,
                                 float sm_scale, float *out, void *ws, size_t ws_bytes,
                                 void *stream);

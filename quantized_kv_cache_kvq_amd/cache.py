@@ -110,7 +110,8 @@ class LayerCache:
     def workspace(self, n_q_heads):
         need = lib.decode_workspace_bytes(self.desc, n_q_heads)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            # zero once: the library keeps its completion counters zero
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def decode(self, q, sm_scale, out=None, body_splits=0, stream=None, ws=None):

@@ -177,14 +177,17 @@ int max_splits(const kvq_layer &L) {
 }
 
 struct WsLayout {
-  size_t qw, qsum, part, total;
+  size_t cnt, qw, qsum, part, total;
 };
 
+// Workspace: split-completion counters (fixed size and place, zero between
+// calls), prepared query, per-block query sums, split partials.
 WsLayout ws_layout(const kvq_layer &L, int Hq, int S) {
   WsLayout w;
   const size_t bh = (size_t)L.batch * Hq;
-  w.qw = 0;
-  w.qsum = align256(bh * KVQ_HEAD_DIM * sizeof(float));
+  w.cnt = 0;
+  w.qw = align256(DECODE_CNT_BYTES);
+  w.qsum = w.qw + align256(bh * KVQ_HEAD_DIM * sizeof(float));
   w.part = w.qsum + align256(bh * 4 * sizeof(float));
   w.total = w.part + align256(bh * (size_t)S * PSTRIDE * sizeof(float));
   return w;
@@ -383,6 +386,9 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
     return fail(KVQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, W.total);
   if ((long long)P.Hkv * P.NHG > 65535 || P.B > 65535)
     return fail(KVQ_ERR_UNSUPPORTED, "grid too large (kv heads x head groups or batch above 65535)");
+  if (units > DECODE_MAX_UNITS)
+    return fail(KVQ_ERR_UNSUPPORTED, "batch x kv heads x head groups = %d above %d", units,
+                DECODE_MAX_UNITS);
 
   uint8_t *wsb = reinterpret_cast<uint8_t *>(ws);
   DecodeArgs a;
@@ -390,6 +396,8 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
   a.k = plane_args(L, L.k);
   a.v = plane_args(L, L.v);
   a.part = reinterpret_cast<float *>(wsb + W.part);
+  a.out = out;
+  a.cnt = reinterpret_cast<unsigned *>(wsb + W.cnt);
   a.B = P.B;
   a.Hkv = P.Hkv;
   a.Hq = P.Hq;

@@ -124,15 +124,6 @@ __global__ __launch_bounds__(64) void lowrank_query_kernel(const float *__restri
   }
 }
 
-// ---------------------------------------------------------------- combine --
-
-// One wave per (batch entry, query head).
-__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a, float *__restrict__ out) {
-  __shared__ float olow[D];
-  const int bh = blockIdx.x;
-  combine_head(a, out, bh / a.Hq, bh % a.Hq, olow);
-}
-
 // --------------------------------------------------------------- launcher --
 
 int decode_tile_tokens(int kcodec, int vcodec, int basis) {
@@ -265,9 +256,7 @@ hipError_t launch_decode(const DecodeArgs &args, const float *q, float sm_scale,
   }
   if (r != hipSuccess) return r;
   if (ev0) timing_commit();
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(64), 0, stream, a, out);
+  (void)out;   // merged into a.out by each unit's last workgroup
   return hipGetLastError();
 }
 

@@ -72,6 +72,26 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// -------------------------------------------- cross-workgroup exchange --
+// Split partials travel between workgroups that may sit on different XCDs
+// (each with its own L2) within one launch.  They are written and read with
+// device-scope relaxed atomics, which the compiler emits as L2-coherent
+// accesses (sc1), so no L2 write-back or invalidate is needed; ordering is
+// by waiting for the stores to complete before the completion counter.
+__device__ __forceinline__ void store_agent(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<unsigned *>(p), __builtin_bit_cast(unsigned, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float *p) {
+  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const unsigned *>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float2 load2_agent(const float *p) {
+  const unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__builtin_bit_cast(float, (unsigned)u), __builtin_bit_cast(float, (unsigned)(u >> 32)));
+}
+
 // ------------------------------------------------------------- unpacking --
 
 // Field of BITS bits at compile-time bit offset `bit` of a register array.
@@ -714,10 +734,10 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
       L = fmaf(wt, src[1], L);
     }
     float *dst = io.part + h * io.part_head_stride;
-    dst[4 + c] = o;
+    store_agent(dst + 4 + c, o);
     if (c == 0) {
-      dst[0] = M;
-      dst[1] = L;
+      store_agent(dst, M);
+      store_agent(dst + 1, L);
     }
   }
 }
@@ -803,7 +823,7 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
   // loads in flight per step.
   float mb = NEG_INF, mt = NEG_INF;
   for (int s = lane; s < S; s += 64) {
-    const float m = pr[(long long)s * PSTRIDE];
+    const float m = load_agent(pr + (long long)s * PSTRIDE);
     if (s < Sb) mb = fmaxf(mb, m); else mt = fmaxf(mt, m);
   }
 #pragma unroll
@@ -816,7 +836,7 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
     const int s = s0 + lane;
     float wgt = 0.f;
     if (s < S) {
-      const float2 ml = *reinterpret_cast<const float2 *>(pr + (long long)s * PSTRIDE);
+      const float2 ml = load2_agent(pr + (long long)s * PSTRIDE);
       const float M = s < Sb ? mb : mt;
       wgt = ml.x == NEG_INF ? 0.f : exp2f(ml.x - M);
       if (s < Sb) lb = fmaf(wgt, ml.y, lb); else lt = fmaf(wgt, ml.y, lt);
@@ -827,7 +847,7 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int i = i0 + k < cnt ? i0 + k : cnt - 1;
-        v[k] = *reinterpret_cast<const float2 *>(pr + (long long)(s0 + i) * PSTRIDE + 4 + 2 * lane);
+        v[k] = load2_agent(pr + (long long)(s0 + i) * PSTRIDE + 4 + 2 * lane);
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -889,6 +909,26 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
   reinterpret_cast<float2 *>(out + bh * D)[lane] = o;
 }
 
+// After a split's partials are stored: count the split as finished (one
+// device-scope counter per unit in the workspace); the workgroup that
+// finishes its unit last merges the unit's heads (wave w takes head w of
+// the group) and re-arms the counter, so counters are zero between calls.
+__device__ inline void finish_split(const DecodeArgs &a, int b, int kvh, int hg, uint8_t *lds) {
+  __shared__ unsigned s_last;
+  __builtin_amdgcn_s_waitcnt(0);           // this thread's partial stores completed
+  __syncthreads();
+  unsigned *cnt = a.cnt + ((long long)b * a.Hkv + kvh) * a.NHG + hg;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(a.S_total - 1);
+  __syncthreads();
+  if (!s_last) return;
+  const int w = threadIdx.x >> 6;
+  if (w < a.HG)
+    combine_head(a, a.out, b, kvh * a.G + hg * a.HG + w, reinterpret_cast<float *>(lds) + w * D);
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Plain / KVarN body with fixed codecs, plus the binary16 tail splits in
 // the same launch (so the short tail work overlaps the body).  Grid:
 // x = split (tail splits first, then body splits), y = kv head * NHG +
@@ -912,6 +952,7 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs
   int b, kvh, hg, s;
   if (split_decode(a, b, kvh, hg, s)) run_tail<HG>(a, b, kvh, hg, s, lds);
   else run_body<CB>(a, b, kvh, hg, s, lds);
+  finish_split(a, b, kvh, hg, lds);
 }
 
 // Low-rank body: per-head (codec, rank) chosen at run time among the
@@ -942,6 +983,7 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(De
     KVQ_LR_CASES(KVQ_LR_DISPATCH) {}
 #undef KVQ_LR_DISPATCH
   }
+  finish_split(a, b, kvh, hg, lds);
 }
 
 inline bool decode_lowrank_supported_impl(int codec, int rank) {

@@ -538,10 +538,10 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
       L = fmaf(wt, src[1], L);
     }
     float *dst = io.part + h * io.part_head_stride;
-    dst[4 + c] = o;
+    store_agent(dst + 4 + c, o);
     if (c == 0) {
-      dst[0] = M;
-      dst[1] = L;
+      store_agent(dst, M);
+      store_agent(dst + 1, L);
     }
   }
 }

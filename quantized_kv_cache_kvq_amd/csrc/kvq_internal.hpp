@@ -27,6 +27,8 @@ struct DecodeArgs {
   float scale_body;       // multiplier taking body scores to the log2 domain
   float scale_tail;
   float *part;            // [B][Hq][S_total][PSTRIDE]
+  float *out;             // [B][Hq][128] final output
+  unsigned *cnt;          // [B][Hkv][NHG] finished-split counters (zero between calls)
   int B, Hkv, Hq, G, HG, NHG;
   int body_tokens, tail_tokens;
   int S_body, S_tail, S_total;
@@ -54,6 +56,9 @@ void timing_commit();
 // Split-K decode workgroups: waves per workgroup and workgroups resident
 // per CU (the split policy sizes one round of workgroups from these).
 constexpr int DECODE_WG_WAVES = 8;
+// Completion counters at the start of every decode workspace.
+constexpr int DECODE_MAX_UNITS = 16384;
+constexpr size_t DECODE_CNT_BYTES = DECODE_MAX_UNITS * sizeof(unsigned);
 constexpr int DECODE_WG_PER_CU = 1;
 
 int decode_tile_tokens(int kcodec, int vcodec, int basis);

@@ -114,3 +114,35 @@ def test_uniform_keys_give_value_mean(gpu):
     out = cache.decode(synth.queries(wl, 0).to(gpu), 1.0).cpu().numpy()
     vq = OL.attention_kv(OL.encode_plane(v, ov), None, ov, 300, 0)
     assert np.max(np.abs(out[0] - vq[0, :, 0, :].mean(0))) < 1e-4
+
+
+def test_workspace_reuse_across_calls_and_shapes(gpu):
+    """Splits of one call are merged by whichever workgroup finishes its
+    unit last, through the workspace; consecutive calls (new queries, other
+    split counts, another layer shape) on one workspace must each see only
+    their own partials."""
+    wl = synth.WORKLOADS["gqa4_q8k_q4v_tail1024"]
+    ws = None
+    for T, N, Hq, splits in [(3000, 1024, 32, 0), (2049, 128, 32, 7), (700, 0, 8, 0),
+                             (3000, 1024, 32, 3), (1300, 256, 16, 0)]:
+        w = wl.with_(T=T, N=N, Hq=Hq)
+        k = synth.layer_rows(w, 0, "k").numpy()
+        v = synth.layer_rows(w, 0, "v").numpy()
+        gk, gv, ok_, ov = H.specs(w)
+        cache = H.new_cache(w, 3072, gk, gv, gpu, N=N)
+        kenc, kp, kt = H.oracle_layer_bytes(k, ok_, 3072, N)
+        venc, vp, vt = H.oracle_layer_bytes(v, ov, 3072, N)
+        H.upload(cache, "k", kp, kt)
+        H.upload(cache, "v", vp, vt)
+        cache.n_tokens = T
+        need = cache.workspace(Hq).numel()
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 1 << 24), dtype=torch.uint8, device=gpu)
+        for step in range(3):
+            q = synth.queries(w, 0, step=step)
+            ref = OL.decode(q.numpy(), kenc, venc, OL.tail_ring(k, N) if N else None,
+                            OL.tail_ring(v, N) if N else None, ok_, ov, T, N, w.sm_scale)
+            out = cache.decode(q.to(gpu), w.sm_scale, body_splits=splits, ws=ws)
+            torch.cuda.synchronize()
+            err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))
+            assert err <= H.ATOL, (T, N, Hq, splits, step, err)
