@@ -193,8 +193,10 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     if (nb == 2) return make_uint2(*reinterpret_cast<const uint32_t *>(p), 0u);
     return make_uint2((uint32_t)*p, 0u);
   };
-  auto load_k_nt = [&](int t0, int nt) {
-    const int tok = min(16 * nt + n, t_end - 1 - t0);
+  // lim: last valid in-tile position (0 for the dummy prefetch after the
+  // last tile, which then reads one line per chunk, an L2 hit)
+  auto load_k_nt = [&](int t0, int lim, int nt) {
+    const int tok = min(16 * nt + n, lim);
     const uint8_t *tile = io.kcodes + (unsigned)t0 * Q::RK;
 #pragma unroll
     for (int j = 0; j < NKB; ++j) kr[nt][j] = kq_load<Q>(tile, tok, j, g);
@@ -203,8 +205,8 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     vsr[nt] = side(io.vsc, t0 + tok, NBV);
     if constexpr (C::VFAM == FAM_1) vmr[nt] = side(io.vmn, t0 + tok, NBV);
   };
-  auto load_v = [&](int t0) {
-    const int tok = min(lane, t_end - 1 - t0);
+  auto load_v = [&](int t0, int lim) {
+    const int tok = min(lane, lim);
     const uint8_t *tile = io.vcodes + (unsigned)t0 * Q::RV;
     constexpr int CV = Q::CV, NCV = Q::RV / CV;
 #pragma unroll
@@ -229,15 +231,16 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   };
 
   // The first tile's loads go out before the query work below.  Loads are
-  // unconditional (a wave without tiles reads its split's first tile, and
-  // the last tile's prefetch re-reads the current tile, an L2 hit), so the
+  // unconditional (a wave without tiles, and the prefetch after the last
+  // tile, read only token 0 of a valid tile), so the
   // compiler can count outstanding loads exactly and never has to drain
   // the prefetched tile early.
   {
     const int lt0 = first < t_end ? first : (int)io.t_begin;
+    const int lim0 = first < t_end ? t_end - 1 - lt0 : 0;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) load_k_nt(lt0, nt);
-    load_v(lt0);
+    for (int nt = 0; nt < NT; ++nt) load_k_nt(lt0, lim0, nt);
+    load_v(lt0, lim0);
   }
   __builtin_amdgcn_sched_barrier(0);    // keep the tile loads ahead of the query work
 
@@ -311,6 +314,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
 
   for (int t0 = first; t0 < t_end; t0 += stride) {
     const int tn = t0 + stride < t_end ? t0 + stride : t0;   // prefetch target
+    const int limn = t0 + stride < t_end ? t_end - 1 - tn : 0;
     const int lim = t_end - 1 - t0;
 
     // ---- value row of token `lane` into LDS as offset-binary bytes; byte
@@ -345,7 +349,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     uint2 vs_cur[NT], vm_cur[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) { vs_cur[nt] = vsr[nt]; vm_cur[nt] = vmr[nt]; }
-    load_v(tn);
+    load_v(tn, limn);
 
     // ---- QK on the integer matrix cores
     float sc[HGRP][NT];
@@ -362,7 +366,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
         if constexpr (KB == 8 && C::KFAM == FAM_1) { bb.x ^= 0x80808080u; bb.y ^= 0x80808080u; }
         kb[j] = (long)((uint64_t)bb.x | ((uint64_t)bb.y << 32));
       }
-      load_k_nt(tn, nt);                // N-tile nt's registers are free again
+      load_k_nt(tn, limn, nt);          // N-tile nt's registers are free again
       const bool valid = 16 * nt + n <= lim;
 #pragma unroll
       for (int rg = 0; rg < HGRP; ++rg) {
