@@ -170,16 +170,25 @@ def cpu_baseline(wl, reps_layers, budget_s=12.0):
 
 
 def kernel_source_hash():
-    """sha256 over the HIP sources and headers the kernels are built from."""
+    """sha256 over the HIP sources and headers the kernels are built from,
+    with comments and whitespace removed (edits to comments do not change
+    the kernels)."""
     import hashlib
+    import re
+
+    def code(path):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        return " ".join(text.split()).encode()
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_kvq_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".h")):
             h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "kvq.h"), "rb").read())
+            h.update(code(os.path.join(csrc, name)))
+    h.update(code(os.path.join(ROOT, "include", "kvq.h")))
     return h.hexdigest()[:16]
 
 

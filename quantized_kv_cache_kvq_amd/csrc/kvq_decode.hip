@@ -1,30 +1,16 @@
-// Decode attention over the packed cache: split-K flash-decode with the
-// dequantisation done in registers.
+// Decode attention over the packed cache: query pre-transforms, the launch
+// of the split-K decode kernel (kvq_decode_impl.hpp, kvq_decode_q.hpp) and
+// its event-timing hook.
 //
 // The computation (forum thread on decode bandwidth, second post): scores
-// s_t = sm_scale <q, k_t>, softmax over t, output sum_t p_t v_t.  The cache
-// is read once per step, so the kernel is bound by HBM bandwidth (same
-// thread, first post).  Design for gfx950:
-//
-//  * Grid: one 256-thread workgroup per (batch entry, kv head, head group of
-//    HG query heads sharing it, context split).  Splits cover the quantised
-//    body and the binary16 precision tail; each writes an (m, l, o) partial.
-//  * QK, token per thread: the 64-token tiled row layout makes "thread t
-//    loads token t's row" a run of fully coalesced 16-byte loads (a wave
-//    reads 1 KB contiguous per instruction).  The codes are unpacked in
-//    registers; the HG query vectors are wave-uniform, so the compiler keeps
-//    them in scalar registers and every multiply-add takes one from there.
-//    Block scales are folded in once per 32-block: s += d_j * sum_i q_i c_i
-//    (+ m_j * sum_i q_i for _1 codes).
-//  * Online softmax in the log2 domain (scores pre-multiplied by log2 e);
-//    the tile maximum is a wave shuffle reduction plus one LDS exchange.
-//  * PV: the value tile is staged raw (packed) in LDS with the p*d_j
-//    weights; thread (slot, group) then owns 8 output channels and walks the
-//    tile's tokens, unpacking its 8 codes per token and accumulating HG x 8
-//    outputs.  A cross-slot reduction through LDS closes each split.
-//  * A second kernel combines the splits: M = max m_s, L = sum l_s 2^(m_s-M),
-//    o = sum o_s 2^(m_s-M) / L, after taking body partials back to the raw
-//    basis (inverse Hadamard and 1/w for KVarN, P_h for low rank).
+// s_t = sm_scale <q, k_t>, softmax over t, output sum_t p_t v_t; the cache is
+// read once per step, so the step is bound by HBM bandwidth (same thread,
+// first post).  One launch does all of it: workgroups own context splits of
+// a (batch entry, kv head, head group), write (m, l, o) partials, and the
+// workgroup that finishes a unit last merges the splits (M = max m_s,
+// L = sum l_s 2^(m_s - M), o = sum o_s 2^(m_s - M) / L) after taking body
+// partials back to the raw basis (inverse Hadamard and 1/w for KVarN, P_h
+// for low rank).
 #include <vector>
 
 #include "kvq_decode_impl.hpp"

@@ -1,26 +1,20 @@
-// Device implementation of the split-K decode kernel (design notes in
-// kvq_decode.hip).  Included by the per-head-group instantiation units.
+// Device implementation of the split-K decode kernel.  Included by the
+// per-head-group instantiation units.
 //
-// Work decomposition: a 256-thread workgroup owns one context split of one
-// (batch entry, kv head, group of HG <= 8 query heads).  Its four waves are
+// Work decomposition: a workgroup of NWAVE waves owns one context split of
+// one (batch entry, kv head, group of HG <= 8 query heads).  Its waves are
 // independent flash-decoders: each walks its own 64-token tiles of the split
 // with its own running max, sum and output accumulators, so the main loop
-// has no workgroup barrier.  The four wave states are merged through LDS
-// once, at the end of the split.
+// has no workgroup barrier.  The wave states are merged through LDS once, at
+// the end of the split, and the split's partial is stored for the unit's
+// final merge (combine_head, run by the unit's last workgroup).
 //
-// Per 64-token tile, one wave does:
-//   QK on the matrix cores: v_mfma_f32_16x16x32_f16 with the query as the A
-//     operand (rows = query heads) and 16 tokens x 32 channels of codes as
-//     the B operand.  Codes are small integers, exact in binary16; the
-//     binary32 query is split into hi + lo binary16 parts (two MFMAs into
-//     one accumulator), after a per-head power-of-two rescale, which keeps
-//     ~22 significant bits.  Block scales are applied to the fp32 results:
-//     s = sum_j d_j * C_j (+ m_j * sum(q over block j) for _1 codes).
-//   Online softmax in the log2 domain (DPP row reductions).
-//   PV on the vector units: value rows are staged raw in LDS with the
-//     p * d_j weights; lane (slot, group) owns 8 output channels.
-// The next tile's code loads are issued while the current tile is still
-// being computed (one tile of register prefetch).
+// Quantised bodies run attend_q (kvq_decode_q.hpp: QK on the integer matrix
+// cores, PV on binary16 MFMA).  The binary16 precision tail and F16 codecs
+// run attend_range below: QK on v_mfma_f32_16x16x32_f16 with the query split
+// into hi + lo binary16 parts (rows (head, part)), online softmax in the
+// log2 domain with DPP row reductions, PV on the matrix cores with the
+// weights staged in LDS and read back transposed.
 #pragma once
 
 #include <hip/hip_ext.h>
