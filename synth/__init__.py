@@ -4,8 +4,10 @@ Shared by the tests, the smoke check and the benchmark.  This module draws
 random numbers and arranges them into tensors; it holds none of the codec,
 rotation, projection or attention arithmetic.  Every chunk (one batch entry,
 one kv head, one of K/V/q, one layer) has its own seed derived from the
-workload seed and the chunk's key, so any chunk can be regenerated alone
-(e.g. on the host for the oracle while the device generates the rest).
+workload seed and the chunk's key, so any chunk can be regenerated alone.
+Chunks regenerate identically on the same device type (torch's host and
+GPU generators differ): tests that generate on the device hand the device's
+values to the oracle.
 
 The five workloads stand in for the pages' own (a 27B model's 64k-context
 cache, an 8-KV-head 32-layer Llama-class cache, Wikitext/LongBench text),
