@@ -225,6 +225,88 @@ def copy_probe(nbytes, reps):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def prefill(args, dev):
+    """Prefill-scale append and transcode (the survey's next-row workload):
+    append the whole context of one layer in one call into an empty cache,
+    and transcode a full binary16 layer to q8_0.  Reports each kernel's
+    bytes moved (inputs read + packed rows, scales, mins and tail written;
+    transcode: source read + destination written) per second against the
+    8 TB/s HBM peak."""
+    wl = synth.WORKLOADS[args.workload]
+    kc, vc = (wl.kcodec, wl.vcodec) if wl.layers == 1 else ("q8_0", "q8_0")
+    ks, vs = plane_specs(wl, 0, None if wl.layers == 1 else kc)
+    capacity = math.ceil(wl.T / 64) * 64
+    k = synth.layer_rows(wl, 0, "k", device=dev)
+    v = synth.layer_rows(wl, 0, "v", device=dev)
+    reps = 3
+    caches = [LayerCache(wl.B, wl.Hkv, capacity, wl.N, ks, vs, dev) for _ in range(reps)]
+
+    def plane_out(c):
+        tot = 0
+        for name in ("k", "v"):
+            for key, t in c.bufs[name].items():
+                if t is not None and not (key == "tail" and c.tail_len == 0):
+                    tot += t.numel() * t.element_size()
+        return tot
+
+    out_bytes = plane_out(caches[0]) * wl.T / capacity
+    in_bytes = 2 * k.numel() * 4
+    stream = torch.cuda.current_stream(dev)
+    for c in caches:
+        c.n_tokens = 0
+        c.append(k, v)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(3, args.steps // 20)
+    e0.record(stream)
+    for i in range(n):
+        c = caches[i % reps]
+        c.n_tokens = 0
+        c.append(k, v)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    app_ms = e0.elapsed_time(e1) / n
+    app_gbs = (in_bytes + out_bytes) / (app_ms * 1e-3) / 1e9
+    del caches
+    tr = None
+    if wl.basis != "lowrank":
+        tr = transcode_rate(wl, ks, vs, capacity, k, v, plane_out, n, dev, stream)
+    line = {
+        "metric": "prefill append and layer transcode GB/s (bytes read + written)",
+        "append": {"value": round(app_gbs, 1), "unit": "GB/s", "ms": round(app_ms, 4),
+                   "bytes": int(in_bytes + out_bytes), "frac_of_hbm_peak": round(app_gbs / HBM_PEAK_GBS, 4),
+                   "tokens_per_s": round(wl.B * wl.T / (app_ms * 1e-3), 1)},
+        "transcode_f16_to_q8_0": tr,
+        "config": {"workload": wl.name, "batch": wl.B, "kv_heads": wl.Hkv, "context": wl.T,
+                   "tail": wl.N, "k_codec": kc or "per-head", "v_codec": vc or "per-head",
+                   "basis": wl.basis},
+        "n_gpus": 1, "data": "synthetic (seeded), resident in HBM",
+    }
+    print(json.dumps(line), flush=True)
+
+
+def transcode_rate(wl, ks, vs, capacity, k, v, plane_out, n, dev, stream):
+    """Full binary16 layer re-encoded to q8_0 (the degrade step) n times."""
+    src = LayerCache(wl.B, wl.Hkv, capacity, 0, PlaneSpec("f16", ks.basis, ks.w),
+                     PlaneSpec("f16", vs.basis, vs.w), dev)
+    src.append(k, v)
+    dst = LayerCache(wl.B, wl.Hkv, capacity, 0, PlaneSpec("q8_0", ks.basis, ks.w),
+                     PlaneSpec("q8_0", vs.basis, vs.w), dev)
+    src.transcode_into(dst)
+    torch.cuda.synchronize()
+    tr_bytes = (plane_out(src) + plane_out(dst)) * wl.T / capacity
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        src.transcode_into(dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tr_ms = e0.elapsed_time(e1) / n
+    tr_gbs = tr_bytes / (tr_ms * 1e-3) / 1e9
+    return {"value": round(tr_gbs, 1), "unit": "GB/s", "ms": round(tr_ms, 4), "bytes": int(tr_bytes),
+            "frac_of_hbm_peak": round(tr_gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +315,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=synth.ORDER)
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure prefill-scale append and layer transcode instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -246,6 +330,9 @@ def main():
         return
     lib.load()
     dev = torch.device("cuda:0")
+    if args.prefill:
+        prefill(args, dev)
+        return
     wl = synth.WORKLOADS[args.workload]
     if wl.name == "tiny":
         wl = wl.with_(T=256)

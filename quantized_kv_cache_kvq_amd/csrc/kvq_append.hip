@@ -1,10 +1,11 @@
 // Append kernel: rotate / project, block-quantise, bit-pack and store new
 // tokens, plus their binary16 precision-tail copy.
 //
-// One wave (64 lanes) per (batch entry, new token, kv head, K|V).  Lane l
-// owns raw channels 2l, 2l+1.  Steps, after the BeeLlama v0.4.0 notes (KVarN
-// and precision-tail sections) and the KV-COBRA explainer (projection with
-// the Hadamard rotation fused in):
+// One wave (64 lanes) per item = (batch entry, new token, kv head, K|V);
+// 4-wave workgroups stride over the items.  Lane l owns raw channels 2l,
+// 2l+1.  Steps, after the BeeLlama v0.4.0 notes (KVarN and precision-tail
+// sections) and the KV-COBRA explainer (projection with the Hadamard
+// rotation fused in):
 //   1. tail copy: RN16 of the raw vector into ring slot t mod tail_len;
 //   2. stored coordinates: x (plain), H (x * w) by an in-wave fast
 //      Walsh-Hadamard transform (hadamard), or P_h^T x (low rank);
@@ -53,30 +54,44 @@ __device__ inline void fwht128_wave(float &a, float &b) {
   }
 }
 
-__global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
-                                                    const float *__restrict__ k_new,
-                                                    const float *__restrict__ v_new, int n_new,
-                                                    int t0) {
-  __shared__ float xin[D];
-  __shared__ float coords[D];
-  __shared__ uint8_t codes[D];
-  __shared__ float s_scale[4];
-  __shared__ float s_min[4];
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-  int id = blockIdx.x;
+// Source row of an item = (batch entry, new token, kv head, K|V).
+__device__ __forceinline__ const float *item_src(const PlaneArgs &kp, const float *__restrict__ k_new,
+                                                 const float *__restrict__ v_new, int n_new,
+                                                 unsigned item) {
+  unsigned id = item;
+  const int which = id & 1;
+  id >>= 1;
+  const unsigned hkv = (unsigned)kp.hkv;
+  const unsigned h = id % hkv;
+  id /= hkv;
+  const unsigned i = id % (unsigned)n_new;
+  const unsigned b = id / (unsigned)n_new;
+  return (which ? v_new : k_new) + (((long long)b * n_new + i) * hkv + h) * D;
+}
+
+// One item, one wave; x = this lane's two raw channels (loaded by the
+// caller ahead of time).  The LDS arrays are this wave's own.
+__device__ void append_item(const PlaneArgs &kp, const PlaneArgs &vp, int n_new, int t0,
+                            unsigned item, float2 x, float *xin, float *coords, uint8_t *codes,
+                            float *s_scale, float *s_min) {
+  unsigned id = item;
   const int which = id & 1;
   id >>= 1;
   const PlaneArgs &p = which ? vp : kp;
   const int hkv = p.hkv;
-  const int h = id % hkv;
-  id /= hkv;
-  const int i = id % n_new;
-  const int b = id / n_new;
+  const int h = (int)(id % (unsigned)hkv);
+  id /= (unsigned)hkv;
+  const int i = (int)(id % (unsigned)n_new);
+  const int b = (int)(id / (unsigned)n_new);
   const int t = t0 + i;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
 
-  const float *src = (which ? v_new : k_new) + (((long long)b * n_new + i) * hkv + h) * D;
-  float2 x = reinterpret_cast<const float2 *>(src)[lane];
 
   // 1. precision tail: binary16 raw copy, slot t mod N, 256-byte rows.  Only
   //    the newest N tokens of this call write: older ones in the same call
@@ -103,7 +118,7 @@ __global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
   } else if (p.basis == KVQ_BASIS_LOWRANK) {
     xin[2 * lane] = x.x;
     xin[2 * lane + 1] = x.y;
-    __syncthreads();
+    wave_sync();
     const uint16_t *P = p.proj + (long long)h * D * D;
     for (int k = lane; k < g.n; k += 64) {
       float acc = 0.f;
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
     coords[2 * lane] = x.x;
     coords[2 * lane + 1] = x.y;
   }
-  __syncthreads();
+  wave_sync();
 
   uint8_t *row_codes = p.codes + g.codes_off;
   const int fam = codec_family(g.codec);
@@ -204,7 +219,7 @@ __global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
       s_min[lane] = m;
     }
   }
-  __syncthreads();
+  wave_sync();
 
   // 4. codes (masked to `bits` bits)
   const uint32_t mask = (1u << bits) - 1u;
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
     }
     codes[e] = (uint8_t)((uint32_t)q & mask);
   }
-  __syncthreads();
+  wave_sync();
 
   // 5. pack: unit u (us bytes) holds row bits [8*us*u, 8*us*(u+1))
   const int us = g.c < 4 ? g.c : 4;
@@ -246,11 +261,43 @@ __global__ __launch_bounds__(64) void append_kernel(PlaneArgs kp, PlaneArgs vp,
   }
 }
 
+// Items strided over a grid of 4-wave workgroups: far fewer workgroups
+// than items, so a prefill-sized append is not bound by workgroup dispatch.
+__global__ __launch_bounds__(256) void append_kernel(PlaneArgs kp, PlaneArgs vp,
+                                                     const float *__restrict__ k_new,
+                                                     const float *__restrict__ v_new, int n_new,
+                                                     int t0, unsigned items) {
+  __shared__ float xin[4][D];
+  __shared__ float coords[4][D];
+  __shared__ uint8_t codes[4][D];
+  __shared__ float s_scale[4][4];
+  __shared__ float s_min[4][4];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const unsigned stride = gridDim.x * 4u;
+  // two items of prefetch per wave (loads past the end re-read the last item)
+  auto load = [&](unsigned it) {
+    const unsigned c = it < items ? it : items - 1;
+    return reinterpret_cast<const float2 *>(item_src(kp, k_new, v_new, n_new, c))[lane];
+  };
+  unsigned item = blockIdx.x * 4u + w;
+  float2 x0 = load(item), x1 = load(item + stride);
+  for (; item < items; item += stride) {
+    const float2 x = x0;
+    x0 = x1;
+    x1 = load(item + 2 * stride);
+    append_item(kp, vp, n_new, t0, item, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+  }
+}
+
 hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
                          const float *v_new, int batch, int n_new, int t0, hipStream_t stream) {
-  const long long blocks = (long long)batch * n_new * kp.hkv * 2;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, kp, vp, k_new,
-                     v_new, n_new, t0);
+  const long long items = (long long)batch * n_new * kp.hkv * 2;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  long long blocks = (items + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kp, vp, k_new,
+                     v_new, n_new, t0, (unsigned)items);
   return hipGetLastError();
 }
 
