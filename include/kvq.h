@@ -181,6 +181,42 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q,
                                        void *ws, size_t ws_bytes, int32_t body_splits,
                                        void *stream);
 
+/* VBR budget controller (VBR announcement thread, opening posts: the cache
+ * stays at 16 bits while it fits, then layers move down a codec ladder in a
+ * profiled per-layer order, never below a floor codec, within a VRAM budget;
+ * any added KV can push a degrade).  Host-only policy; each step it returns
+ * is carried out with kvq_transcode_layer.
+ *
+ * Layer l is stored in codec ladder[level[l]] (K and V alike).  Bytes of a
+ * layer at n tokens: 2 * batch * n_kv_heads * n * (codes + scales + mins of
+ * one 128-wide row) plus, when tail_len > 0, 2 * batch * n_kv_heads *
+ * tail_len * 256 bytes of binary16 tail.  A degrade moves one layer one rung
+ * down; the layer moved next is the one at the highest rung (smallest level)
+ * still above `floor`, ties broken by `order` (a permutation of the layers,
+ * first = degraded first).  Layers never move back up. */
+typedef struct kvq_vbr_policy {
+    int32_t n_layers;
+    const int32_t *ladder;      /* host [ladder_len] kvq_codec, best first */
+    int32_t ladder_len;
+    int32_t floor;              /* lowest allowed ladder index */
+    const int32_t *order;       /* host [n_layers] degrade order */
+    int32_t batch, n_kv_heads, tail_len;
+    long long budget_bytes;
+} kvq_vbr_policy;
+
+/* Bytes of the whole cache at `level` and n_tokens (-1 on bad arguments). */
+long long kvq_vbr_bytes(const kvq_vbr_policy *pol, const int32_t *level, int32_t n_tokens);
+
+/* Degrade steps that make n_tokens fit the budget.  level: host [n_layers],
+ * in/out (updated to the plan).  steps: host [max_steps][3] receives
+ * (layer, from codec, to codec) in the order to run them; *n_steps their
+ * count.  KVQ_OK: fits.  KVQ_ERR_CAPACITY: does not fit even with every
+ * layer at the floor (level and steps hold the floor plan).
+ * KVQ_ERR_WORKSPACE: max_steps too small (the steps so far are valid).
+ * KVQ_ERR_INVALID_ARG: bad policy, level or order; nothing changed. */
+kvq_status kvq_vbr_plan(const kvq_vbr_policy *pol, int32_t n_tokens, int32_t *level,
+                        int32_t *steps, int32_t max_steps, int32_t *n_steps);
+
 /* Measurement hook (not part of the cache format).  kvq_timing_begin
  * creates 2*capacity host-side hipEvents on the current device; each later
  * kvq_decode_attention* call records one pair on its stream, right before

@@ -21,6 +21,8 @@ Module map (each function cites the passage of the source pages it follows):
 * ``layer``     - one layer's cache: append semantics, precision tail,
                   dequantisation, decode and transcode, built from the above.
 * ``budget``    - bit accounting of the stored formats.
+* ``vbr``       - the VBR budget controller (degrade plan over a codec
+                  ladder under a byte budget).
 * ``allocator`` - per-head rank/bit allocation (intra-head trade, cross-head
                   water-filling) on synthetic spectra.
 

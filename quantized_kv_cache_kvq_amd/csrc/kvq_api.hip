@@ -195,6 +195,13 @@ WsLayout ws_layout(const kvq_layer &L, int Hq, int S) {
 
 }  // namespace
 
+namespace kvq {
+// Status setters for the other host translation units (detail for
+// kvq_last_error).
+kvq_status api_fail(kvq_status s, const char *detail) { return fail(s, "%s", detail); }
+kvq_status api_ok() { return ok(); }
+}  // namespace kvq
+
 extern "C" {
 
 int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }

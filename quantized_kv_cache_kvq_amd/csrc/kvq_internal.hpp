@@ -45,6 +45,10 @@ hipError_t launch_transcode(const PlaneArgs &src, const PlaneArgs &dst, int batc
 hipError_t launch_decode(const DecodeArgs &a, const float *q, float sm_scale, float *qw,
                          float *qsum, float *out, hipStream_t stream, bool prep, bool need_qsum);
 
+// Status with detail for kvq_last_error (host).
+kvq_status api_fail(kvq_status s, const char *detail);
+kvq_status api_ok();
+
 // Event timing of the split-K decode kernel (host side, not thread safe).
 hipError_t timing_begin(int capacity);
 hipError_t timing_end(double *total_ms, int *count);

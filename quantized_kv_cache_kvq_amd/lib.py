@@ -78,6 +78,10 @@ _SIGS = {
                                                    ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
                                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                                    ctypes.c_void_p]),
+    "kvq_vbr_bytes": (ctypes.c_longlong, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]),
+    "kvq_vbr_plan": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32)]),
     "kvq_timing_begin": (ctypes.c_int, [ctypes.c_int32]),
     "kvq_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -155,3 +159,40 @@ def timing_end():
     ms, n = ctypes.c_double(), ctypes.c_int32()
     check(load().kvq_timing_end(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+class kvq_vbr_policy(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("ladder", ctypes.POINTER(ctypes.c_int32)),
+                ("ladder_len", ctypes.c_int32), ("floor", ctypes.c_int32),
+                ("order", ctypes.POINTER(ctypes.c_int32)), ("batch", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("tail_len", ctypes.c_int32),
+                ("budget_bytes", ctypes.c_longlong)]
+
+
+def _i32(values):
+    return (ctypes.c_int32 * max(1, len(values)))(*values)
+
+
+def vbr_policy(ladder, floor, order, batch, n_kv_heads, tail_len, budget_bytes):
+    """Policy descriptor; ladder: codec names best first, floor: a ladder
+    index, order: degrade order (layer indices)."""
+    lad = _i32([CODECS.index(c) for c in ladder])
+    ordr = _i32(list(order))
+    pol = kvq_vbr_policy(len(order), lad, len(ladder), floor, ordr, batch, n_kv_heads, tail_len,
+                         budget_bytes)
+    pol._keep = (lad, ordr)
+    return pol
+
+
+def vbr_bytes(pol, level, n_tokens):
+    return load().kvq_vbr_bytes(ctypes.byref(pol), _i32(level), n_tokens)
+
+
+def vbr_plan(pol, n_tokens, level, max_steps=4096):
+    """(status, new levels, steps [(layer, from codec name, to codec name)])."""
+    lv = _i32(level)
+    steps = (ctypes.c_int32 * (3 * max_steps))()
+    n = ctypes.c_int32()
+    st = load().kvq_vbr_plan(ctypes.byref(pol), n_tokens, lv, steps, max_steps, ctypes.byref(n))
+    out = [(steps[3 * i], CODECS[steps[3 * i + 1]], CODECS[steps[3 * i + 2]]) for i in range(n.value)]
+    return st, [lv[i] for i in range(len(level))], out
