@@ -217,6 +217,27 @@ long long kvq_vbr_bytes(const kvq_vbr_policy *pol, const int32_t *level, int32_t
 kvq_status kvq_vbr_plan(const kvq_vbr_policy *pol, int32_t n_tokens, int32_t *level,
                         int32_t *steps, int32_t max_steps, int32_t *n_steps);
 
+/* KV-COBRA per-head rank and bit allocation (KV-COBRA explainer: C1 picks
+ * rank and bits inside a head, C2 moves budget between heads until each
+ * sits at the same marginal error; "Where the bits actually go" for the
+ * accounting).  Host-only calibration step.
+ *
+ * spectra: host [n_heads][128] binary64 variances of each head's key
+ * directions, largest first (eigenvalues of the key covariance).  A head
+ * at (r, b) costs r*b bits per token and has error
+ *   E = sum_{j >= r} spectra[j] + gamma / (2^b - 1)^2 * sum_{j < r} spectra[j]
+ * (dropped variance plus the rounding noise of a b-bit quantiser on the
+ * kept, Hadamard-flattened coordinates; gamma = 4/3 for a 4-sigma range).
+ * Candidates are every (ranks[i], bits[k]); the total cost must not exceed
+ * budget_bits (bits per token summed over heads, e.g. bpd * 128 * n_heads).
+ * Outputs per head: out_rank, out_bits; *rounds: C2 exchange rounds after
+ * the greedy fill; *total_error: the sum of E.  KVQ_ERR_CAPACITY when even
+ * the cheapest candidates exceed the budget. */
+kvq_status kvq_cobra_allocate(const double *spectra, int32_t n_heads, const int32_t *ranks,
+                              int32_t n_ranks, const int32_t *bits, int32_t n_bits,
+                              long long budget_bits, double gamma, int32_t *out_rank,
+                              int32_t *out_bits, int32_t *rounds, double *total_error);
+
 /* Measurement hook (not part of the cache format).  kvq_timing_begin
  * creates 2*capacity host-side hipEvents on the current device; each later
  * kvq_decode_attention* call records one pair on its stream, right before

@@ -23,8 +23,9 @@ Module map (each function cites the passage of the source pages it follows):
 * ``budget``    - bit accounting of the stored formats.
 * ``vbr``       - the VBR budget controller (degrade plan over a codec
                   ladder under a byte budget).
-* ``allocator`` - per-head rank/bit allocation (intra-head trade, cross-head
-                  water-filling) on synthetic spectra.
+* ``allocator`` - per-head rank/bit allocation: the error model, the exact
+                  optimum (dynamic programming) and the C1/C2
+                  water-filling steps.
 
 Parity status: every function here is pinned by a CPU test in
 ``tests/test_oracle_*.py`` against something other than itself (closed forms,

@@ -41,3 +41,16 @@ def kvarn_weights(samples):
     x = torch.as_tensor(samples, dtype=torch.float64)
     sigma = x.reshape(-1, x.shape[-2], x.shape[-1]).std(dim=1, unbiased=False)
     return (1.0 / sigma).to(torch.float32)
+
+
+def head_spectra(keys):
+    """Variances of each head's key directions, largest first: eigenvalues of
+    the second-moment matrix of calibration keys [T, Hkv, 128] (the input of
+    the per-head rank/bit allocation).  Returns [Hkv, 128] float64 (host)."""
+    x = torch.as_tensor(keys, dtype=torch.float64, device="cpu")
+    out = []
+    for h in range(x.shape[1]):
+        xh = x[:, h, :]
+        ev = torch.linalg.eigvalsh(xh.T @ xh / xh.shape[0])
+        out.append(torch.clamp(ev.flip(0), min=0.0))
+    return torch.stack(out)

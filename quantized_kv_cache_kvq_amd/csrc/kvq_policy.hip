@@ -98,3 +98,181 @@ kvq_status kvq_vbr_plan(const kvq_vbr_policy *pol, int32_t n_tokens, int32_t *le
 }
 
 }  // extern "C"
+
+// ------------------------------------------------ KV-COBRA allocation ------
+//
+// KV-COBRA explainer: a head keeps its top r directions (their dropped
+// variance is lost outright) and stores the kept coordinates with b bits,
+// whose rounding noise falls about 4x per extra bit; C1 chooses (r, b) in a
+// head, C2 moves budget between heads until each sits at the same marginal
+// error (water-filling: a bit goes where it removes the most error), and
+// the paper's C2 settles within five rounds.  Error model (the reading the
+// tests pin with the explainer's worked example): with the kept directions
+// flattened by the fused Hadamard rotation, a b-bit uniform quantiser over a
+// 4-sigma range adds gamma / (2^b - 1)^2 of the kept variance, gamma = 4/3.
+//
+// C1: every head's candidate pairs, reduced to the lower convex hull of
+// (bits, error).  C2: start every head at its cheapest hull point, then give
+// hull steps to the head with the largest error drop per bit while the
+// budget lasts; then rounds of exchanges over all candidate pairs (a donor
+// head moves down, the freed bits and any slack let another head move up)
+// until no exchange lowers the total error.
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+namespace {
+
+struct CobraOpt {
+  long long cost;
+  double err;
+  int r, b;
+};
+
+// total order: cost, then error, then rank, then bits
+bool cobra_less(const CobraOpt &x, const CobraOpt &y) {
+  if (x.cost != y.cost) return x.cost < y.cost;
+  if (x.err != y.err) return x.err < y.err;
+  if (x.r != y.r) return x.r < y.r;
+  return x.b < y.b;
+}
+
+}  // namespace
+
+extern "C" kvq_status kvq_cobra_allocate(const double *spectra, int32_t n_heads, const int32_t *ranks,
+                                         int32_t n_ranks, const int32_t *bits, int32_t n_bits,
+                                         long long budget_bits, double gamma, int32_t *out_rank,
+                                         int32_t *out_bits, int32_t *rounds, double *total_error) {
+  if (!spectra || !ranks || !bits || !out_rank || !out_bits || n_heads < 1 || n_ranks < 1 ||
+      n_bits < 1 || budget_bits < 0 || !(gamma > 0.0))
+    return kvq::api_fail(KVQ_ERR_INVALID_ARG, "cobra allocate: bad arguments");
+  for (int i = 0; i < n_ranks; ++i)
+    if (ranks[i] < 1 || ranks[i] > 128)
+      return kvq::api_fail(KVQ_ERR_INVALID_ARG, "cobra allocate: ranks must be in [1, 128]");
+  for (int i = 0; i < n_bits; ++i)
+    if (bits[i] < 1 || bits[i] > 16)
+      return kvq::api_fail(KVQ_ERR_INVALID_ARG, "cobra allocate: bits must be in [1, 16]");
+  const int H = n_heads;
+  std::vector<std::vector<CobraOpt>> opt(H), hull(H);
+  for (int h = 0; h < H; ++h) {
+    const double *lam = spectra + (long long)h * 128;
+    double pre[129];
+    pre[0] = 0.0;
+    for (int j = 0; j < 128; ++j) {
+      if (!(lam[j] >= 0.0))
+        return kvq::api_fail(KVQ_ERR_INVALID_ARG, "cobra allocate: spectra must be non-negative");
+      pre[j + 1] = pre[j] + lam[j];
+    }
+    for (int i = 0; i < n_ranks; ++i)
+      for (int k = 0; k < n_bits; ++k) {
+        const int r = ranks[i], b = bits[k];
+        const double q = std::ldexp(1.0, b) - 1.0;
+        opt[h].push_back({(long long)r * b, (pre[128] - pre[r]) + gamma / (q * q) * pre[r], r, b});
+      }
+    std::vector<CobraOpt> o = opt[h];
+    std::sort(o.begin(), o.end(), cobra_less);
+    // efficient frontier, then lower convex hull
+    std::vector<CobraOpt> f;
+    for (const auto &x : o)
+      if (f.empty() || x.err < f.back().err) {
+        if (!f.empty() && f.back().cost == x.cost) f.back() = x;
+        else f.push_back(x);
+      }
+    for (const auto &x : f) {
+      while (hull[h].size() >= 2) {
+        const CobraOpt &a = hull[h][hull[h].size() - 2], &c = hull[h].back();
+        // drop c if it lies on or above the segment a -> x
+        if ((c.err - a.err) * (x.cost - a.cost) >= (x.err - a.err) * (c.cost - a.cost)) hull[h].pop_back();
+        else break;
+      }
+      hull[h].push_back(x);
+    }
+  }
+  // C2 greedy on the hulls
+  std::vector<int> pos(H, 0);
+  long long used = 0;
+  for (int h = 0; h < H; ++h) used += hull[h][0].cost;
+  if (used > budget_bits)
+    return kvq::api_fail(KVQ_ERR_CAPACITY, "cobra allocate: budget below every head's cheapest pair");
+  for (;;) {
+    int best = -1;
+    double gain = 0.0;
+    for (int h = 0; h < H; ++h) {
+      if (pos[h] + 1 >= (int)hull[h].size()) continue;
+      const CobraOpt &a = hull[h][pos[h]], &c = hull[h][pos[h] + 1];
+      if (used + c.cost - a.cost > budget_bits) continue;
+      const double g = (a.err - c.err) / (double)(c.cost - a.cost);
+      if (g > gain) { gain = g; best = h; }
+    }
+    if (best < 0) break;
+    used += hull[best][pos[best] + 1].cost - hull[best][pos[best]].cost;
+    ++pos[best];
+  }
+  std::vector<CobraOpt> cur(H);
+  for (int h = 0; h < H; ++h) cur[h] = hull[h][pos[h]];
+  // exchange rounds over the full candidate sets: per head, candidates by
+  // cost with the best error at or below each cost (a receiver's best
+  // move for given room is one binary search)
+  std::vector<std::vector<CobraOpt>> by_cost(H), pref(H);
+  for (int h = 0; h < H; ++h) {
+    by_cost[h] = opt[h];
+    std::sort(by_cost[h].begin(), by_cost[h].end(), cobra_less);
+    pref[h] = by_cost[h];
+    for (size_t k = 1; k < pref[h].size(); ++k)
+      if (pref[h][k - 1].err <= pref[h][k].err) pref[h][k] = pref[h][k - 1];
+  }
+  auto best_within = [&](int h, long long max_cost, CobraOpt &out) {
+    const auto &v = by_cost[h];
+    size_t lo = 0, hi = v.size();             // first index with cost > max_cost
+    while (lo < hi) {
+      const size_t mid = (lo + hi) / 2;
+      if (v[mid].cost <= max_cost) lo = mid + 1; else hi = mid;
+    }
+    if (lo == 0) return false;
+    out = pref[h][lo - 1];
+    return true;
+  };
+  int nround = 0;
+  for (int it = 0; it < 64; ++it) {
+    bool changed = false;
+    for (int i = 0; i < H; ++i) {
+      double best_delta = -1e-15;
+      int bj = -1;
+      CobraOpt bi_opt{}, bj_opt{};
+      const long long slack = budget_bits - used;
+      for (const auto &di : opt[i]) {
+        if (di.cost > cur[i].cost + slack) continue;
+        const long long room = slack + cur[i].cost - di.cost;   // bits others may take
+        const double d_i = di.err - cur[i].err;
+        if (d_i < best_delta) { best_delta = d_i; bj = i; bi_opt = di; bj_opt = di; }
+        for (int j = 0; j < H; ++j) {
+          if (j == i) continue;
+          CobraOpt uj;
+          if (!best_within(j, cur[j].cost + room, uj)) continue;
+          const double d = d_i + (uj.err - cur[j].err);
+          if (d < best_delta) { best_delta = d; bj = j; bi_opt = di; bj_opt = uj; }
+        }
+      }
+      if (bj >= 0) {
+        used += bi_opt.cost - cur[i].cost;
+        cur[i] = bi_opt;
+        if (bj != i) {
+          used += bj_opt.cost - cur[bj].cost;
+          cur[bj] = bj_opt;
+        }
+        changed = true;
+      }
+    }
+    if (!changed) break;
+    ++nround;
+  }
+  double tot = 0.0;
+  for (int h = 0; h < H; ++h) {
+    out_rank[h] = cur[h].r;
+    out_bits[h] = cur[h].b;
+    tot += cur[h].err;
+  }
+  if (rounds) *rounds = nround;
+  if (total_error) *total_error = tot;
+  return kvq::api_ok();
+}

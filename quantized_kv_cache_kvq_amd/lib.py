@@ -82,6 +82,11 @@ _SIGS = {
     "kvq_vbr_plan": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int32)]),
+    "kvq_cobra_allocate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                          ctypes.c_longlong, ctypes.c_double,
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "kvq_timing_begin": (ctypes.c_int, [ctypes.c_int32]),
     "kvq_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -196,3 +201,18 @@ def vbr_plan(pol, n_tokens, level, max_steps=4096):
     st = load().kvq_vbr_plan(ctypes.byref(pol), n_tokens, lv, steps, max_steps, ctypes.byref(n))
     out = [(steps[3 * i], CODECS[steps[3 * i + 1]], CODECS[steps[3 * i + 2]]) for i in range(n.value)]
     return st, [lv[i] for i in range(len(level))], out
+
+
+def cobra_allocate(spectra, ranks, bits, budget_bits, gamma=4.0 / 3.0):
+    """Per-head (rank, bits) for spectra [H, 128] (largest first).
+    Returns (list of (rank, bits), C2 rounds, total error)."""
+    import numpy as np
+
+    sp = np.ascontiguousarray(spectra, dtype=np.float64)
+    H = sp.shape[0]
+    r_out, b_out = (ctypes.c_int32 * H)(), (ctypes.c_int32 * H)()
+    rounds, tot = ctypes.c_int32(), ctypes.c_double()
+    check(load().kvq_cobra_allocate(sp.ctypes.data, H, _i32(ranks), len(ranks), _i32(bits), len(bits),
+                                    budget_bits, gamma, r_out, b_out, ctypes.byref(rounds),
+                                    ctypes.byref(tot)))
+    return [(r_out[h], b_out[h]) for h in range(H)], rounds.value, tot.value
