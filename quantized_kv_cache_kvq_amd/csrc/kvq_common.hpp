@@ -109,6 +109,17 @@ __host__ __device__ inline HeadGeom head_geom(const PlaneArgs &p, int b, int h) 
   return g;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Load of data that one call streams once (cache codes and scales): marked
+// non-temporal, so the stream does not push reused lines (code, arguments,
+// split partials) out of the caches.
+template <class T>
+__device__ __forceinline__ T ld_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T *>(p));
+}
+
 // Binary16 <-> binary32 with round-to-nearest-even.
 __device__ inline uint16_t f32_to_f16_bits(float x) {
   return __half_as_ushort(__float2half_rn(x));

@@ -213,7 +213,7 @@ __device__ __forceinline__ void k_load(const uint8_t *__restrict__ plane, long l
   if constexpr (C::KFAM == FAM_F16) {
     const int byte = 2 * e0;
     if (in) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(plane + tiled_offset(t, byte / CC, R, CC) + byte % CC);
+      const u32x4 v = ld_stream<u32x4>(plane + tiled_offset(t, byte / CC, R, CC) + byte % CC);
       r.u[0] = v.x; r.u[1] = v.y; r.u[2] = v.z; r.u[3] = v.w;
     } else {
       r.u[0] = r.u[1] = r.u[2] = r.u[3] = 0u;
@@ -221,7 +221,7 @@ __device__ __forceinline__ void k_load(const uint8_t *__restrict__ plane, long l
   } else if constexpr (b == 8) {
     const int byte = e0;
     if (in) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(plane + tiled_offset(t, byte / CC, R, CC) + byte % CC);
+      const u32x2 v = ld_stream<u32x2>(plane + tiled_offset(t, byte / CC, R, CC) + byte % CC);
       r.u[0] = v.x; r.u[1] = v.y;
     } else {
       r.u[0] = r.u[1] = 0u;
@@ -448,10 +448,10 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
         const int k = tp * PCH + kk;
         const uint8_t *p = io.vcodes + tiled_offset(t, k, C::RV, C::CV);
         if constexpr (C::CV == 16) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(p);
+          const u32x4 v = ld_stream<u32x4>(p);
           vw[4 * kk] = v.x; vw[4 * kk + 1] = v.y; vw[4 * kk + 2] = v.z; vw[4 * kk + 3] = v.w;
         } else if constexpr (C::CV == 8) {
-          const uint2 v = *reinterpret_cast<const uint2 *>(p);
+          const u32x2 v = ld_stream<u32x2>(p);
           vw[2 * kk] = v.x; vw[2 * kk + 1] = v.y;
         } else if constexpr (C::CV == 4) {
           vw[kk] = *reinterpret_cast<const uint32_t *>(p);
@@ -754,17 +754,28 @@ struct BodyLds<C, true> {
 // ------------------------------------------------------------- kernels ----
 
 
-template <class C>
+// LR: per-head widths and codecs (low-rank planes, offsets from the head
+// tables); otherwise every plane has the configuration's fixed geometry.
+template <class C, bool LR>
 __device__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
-  const HeadGeom gk = head_geom(a.k, b, kvh), gv = head_geom(a.v, b, kvh);
+  long long kco, kso, vco, vso;
+  if constexpr (LR) {
+    const HeadGeom gk = head_geom(a.k, b, kvh), gv = head_geom(a.v, b, kvh);
+    kco = gk.codes_off; kso = gk.scales_off;
+    vco = gv.codes_off; vso = gv.scales_off;
+  } else {
+    const long long rows = (long long)(b * a.Hkv + kvh) * a.k.capacity;
+    kco = rows * C::RK; kso = rows * C::NBK;
+    vco = rows * C::RV; vso = rows * (C::VFAM == FAM_F16 ? 0 : C::NBV);
+  }
   const int head0 = kvh * a.G + hg * C::HG;
   SplitIO io;
-  io.kcodes = a.k.codes + gk.codes_off;
-  io.ksc = a.k.scales ? a.k.scales + gk.scales_off : nullptr;
-  io.kmn = a.k.mins ? a.k.mins + gk.scales_off : nullptr;
-  io.vcodes = a.v.codes + gv.codes_off;
-  io.vsc = a.v.scales ? a.v.scales + gv.scales_off : nullptr;
-  io.vmn = a.v.mins ? a.v.mins + gv.scales_off : nullptr;
+  io.kcodes = a.k.codes + kco;
+  io.ksc = a.k.scales ? a.k.scales + kso : nullptr;
+  io.kmn = a.k.mins ? a.k.mins + kso : nullptr;
+  io.vcodes = a.v.codes + vco;
+  io.vsc = a.v.scales ? a.v.scales + vso : nullptr;
+  io.vmn = a.v.mins ? a.v.mins + vso : nullptr;
   io.q = a.q_body + ((long long)b * a.Hq + head0) * D;
   io.scale = a.scale_body;
   const long long tps = (long long)a.tps_body * 64;
@@ -812,55 +823,59 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
   const float *pr = a.part + bh * a.S_total * PSTRIDE;
   const int S = a.S_total, Sb = a.S_body;
 
-  // Two passes over the splits: segment maxima first (lane s reads m of
-  // split s), then weights, l sums and the weighted outputs, with 8 output
-  // loads in flight per step.
+  // Batches of up to 32 splits: every (m, l) and output load of a batch is
+  // issued before any of it is used (one round trip to the coherent level
+  // per batch); batches merge online.  Body (s < Sb) and tail splits are
+  // merged separately, their outputs being in different bases.
+  constexpr int NB = 32;
   float mb = NEG_INF, mt = NEG_INF;
-  for (int s = lane; s < S; s += 64) {
-    const float m = load_agent(pr + (long long)s * PSTRIDE);
-    if (s < Sb) mb = fmaxf(mb, m); else mt = fmaxf(mt, m);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mb = fmaxf(mb, __shfl_xor(mb, o, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, o, 64));
-  }
   float lb = 0.f, lt = 0.f, ob0 = 0.f, ob1 = 0.f, ot0 = 0.f, ot1 = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const int s = s0 + lane;
-    float wgt = 0.f;
-    if (s < S) {
-      const float2 ml = load2_agent(pr + (long long)s * PSTRIDE);
-      const float M = s < Sb ? mb : mt;
-      wgt = ml.x == NEG_INF ? 0.f : exp2f(ml.x - M);
-      if (s < Sb) lb = fmaf(wgt, ml.y, lb); else lt = fmaf(wgt, ml.y, lt);
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    const int cnt = S - s0 < NB ? S - s0 : NB;
+    const int sl = s0 + (lane < cnt ? lane : cnt - 1);
+    const float2 ml = load2_agent(pr + (long long)sl * PSTRIDE);
+    float2 v[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int i = k < cnt ? k : cnt - 1;
+      v[k] = load2_agent(pr + (long long)(s0 + i) * PSTRIDE + 4 + 2 * lane);
     }
-    const int cnt = S - s0 < 64 ? S - s0 : 64;
-    for (int i0 = 0; i0 < cnt; i0 += 8) {
-      float2 v[8];
+    const bool own = lane < cnt, body = sl < Sb;
+    float xb = own && body ? ml.x : NEG_INF, xt = own && !body ? ml.x : NEG_INF;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = i0 + k < cnt ? i0 + k : cnt - 1;
-        v[k] = load2_agent(pr + (long long)(s0 + i) * PSTRIDE + 4 + 2 * lane);
-      }
+    for (int o = 32; o > 0; o >>= 1) {
+      xb = fmaxf(xb, __shfl_xor(xb, o, 64));
+      xt = fmaxf(xt, __shfl_xor(xt, o, 64));
+    }
+    // rescale what earlier batches summed to the new segment maxima
+    const float nmb = fmaxf(mb, xb), nmt = fmaxf(mt, xt);
+    const float cb = mb == NEG_INF ? 0.f : exp2f(mb - nmb);
+    const float ct = mt == NEG_INF ? 0.f : exp2f(mt - nmt);
+    lb *= cb; ob0 *= cb; ob1 *= cb;
+    lt *= ct; ot0 *= ct; ot1 *= ct;
+    mb = nmb;
+    mt = nmt;
+    const float M = body ? mb : mt;
+    const float wgt = !own || ml.x == NEG_INF ? 0.f : exp2f(ml.x - M);
+    float pl = body ? wgt * ml.y : 0.f, ql = body ? 0.f : wgt * ml.y;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = i0 + k;
-        const float wi = i < cnt ? __shfl(wgt, i, 64) : 0.f;
-        if (s0 + i < Sb) {
-          ob0 = fmaf(wi, v[k].x, ob0);
-          ob1 = fmaf(wi, v[k].y, ob1);
-        } else {
-          ot0 = fmaf(wi, v[k].x, ot0);
-          ot1 = fmaf(wi, v[k].y, ot1);
-        }
+    for (int o = 32; o > 0; o >>= 1) {
+      pl += __shfl_xor(pl, o, 64);
+      ql += __shfl_xor(ql, o, 64);
+    }
+    lb += pl;
+    lt += ql;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const float wk = __shfl(wgt, k, 64);          // zero past cnt
+      if (s0 + k < Sb) {
+        ob0 = fmaf(wk, v[k].x, ob0);
+        ob1 = fmaf(wk, v[k].y, ob1);
+      } else {
+        ot0 = fmaf(wk, v[k].x, ot0);
+        ot1 = fmaf(wk, v[k].y, ot1);
       }
     }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lb += __shfl_xor(lb, o, 64);
-    lt += __shfl_xor(lt, o, 64);
   }
 
   // body sum back to the raw basis
@@ -938,14 +953,28 @@ __device__ inline bool split_decode(const DecodeArgs &a, int &b, int &kvh, int &
   return tail;
 }
 
+// The arguments a workgroup reads before its first tile load, fetched in
+// one batch of scalar loads at entry: the argument lines are cold at every
+// launch, and loads issued behind branches would each pay that latency.
+__device__ __forceinline__ void fetch_args(const DecodeArgs &a) {
+  asm volatile("" ::"s"(a.S_tail), "s"(a.S_body), "s"(a.S_total), "s"(a.NHG), "s"(a.G),
+               "s"(a.Hkv), "s"(a.Hq), "s"(a.body_tokens), "s"(a.tail_tokens), "s"(a.tps_body),
+               "s"(a.tps_tail), "s"(a.scale_body), "s"(a.scale_tail), "s"(a.q_body),
+               "s"(a.q_tail), "s"(a.part));
+  asm volatile("" ::"s"(a.k.codes), "s"(a.k.scales), "s"(a.k.mins), "s"(a.k.tail),
+               "s"(a.k.capacity), "s"(a.k.tail_len), "s"(a.v.codes), "s"(a.v.scales),
+               "s"(a.v.mins), "s"(a.v.tail));
+}
+
 template <int HG, int KC, int VC>
 __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs a) {
   using CB = Cfg<HG, KC, VC, D, D>;
   using CT = Cfg<HG, KVQ_F16, KVQ_F16, D, D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax<BodyLds<CB>::bytes, CT::LDS_BYTES>::value];
   int b, kvh, hg, s;
+  fetch_args(a);
   if (split_decode(a, b, kvh, hg, s)) run_tail<HG>(a, b, kvh, hg, s, lds);
-  else run_body<CB>(a, b, kvh, hg, s, lds);
+  else run_body<CB, false>(a, b, kvh, hg, s, lds);
   finish_split(a, b, kvh, hg, lds);
 }
 
@@ -968,12 +997,13 @@ template <int HG>
 __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LrLds<HG>::bytes];
   int b, kvh, hg, s;
+  fetch_args(a);
   if (split_decode(a, b, kvh, hg, s)) {
     run_tail<HG>(a, b, kvh, hg, s, lds);
   } else {
     const int codec = a.k.hcodec[kvh], rank = a.k.hrank[kvh];
 #define KVQ_LR_DISPATCH(CC, RR)                                                           \
-    if (codec == CC && rank == RR) run_body<Cfg<HG, CC, CC, RR, RR>>(a, b, kvh, hg, s, lds); else
+    if (codec == CC && rank == RR) run_body<Cfg<HG, CC, CC, RR, RR>, true>(a, b, kvh, hg, s, lds); else
     KVQ_LR_CASES(KVQ_LR_DISPATCH) {}
 #undef KVQ_LR_DISPATCH
   }

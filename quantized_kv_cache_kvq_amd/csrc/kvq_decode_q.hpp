@@ -120,21 +120,22 @@ __device__ __forceinline__ uint64_t kq_load(const uint8_t *__restrict__ tile, in
   if constexpr (B == 8 || B == 4 || B == 2 || B == 1) {
     const uint8_t *p = tile + (unsigned)((b0 / CK) * (TILE * CK) + tok * CK + b0 % CK);
     if constexpr (B == 8) {
-      const uint2 v = *reinterpret_cast<const uint2 *>(p);
+      const u32x2 v = ld_stream<u32x2>(p);
       return (uint64_t)v.x | ((uint64_t)v.y << 32);
     } else if constexpr (B == 4) {
-      return *reinterpret_cast<const uint32_t *>(p);
+      return ld_stream<uint32_t>(p);
     } else if constexpr (B == 2) {
-      return *reinterpret_cast<const uint16_t *>(p);
+      return ld_stream<uint16_t>(p);
     } else {
-      return *p;
+      return ld_stream<uint8_t>(p);
     }
   } else {
     uint64_t w = 0;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       const int b = b0 + i;
-      w |= (uint64_t)tile[(unsigned)((b / CK) * (TILE * CK) + tok * CK + b % CK)] << (8 * i);
+      w |= (uint64_t)ld_stream<uint8_t>(tile + (unsigned)((b / CK) * (TILE * CK) + tok * CK + b % CK))
+           << (8 * i);
     }
     return w;
   }
@@ -189,9 +190,12 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
 
   auto side = [&](const uint16_t *base, int t, int nb) -> uint2 {
     const uint16_t *p = base + (unsigned)(t * nb);
-    if (nb == 4) return *reinterpret_cast<const uint2 *>(p);
-    if (nb == 2) return make_uint2(*reinterpret_cast<const uint32_t *>(p), 0u);
-    return make_uint2((uint32_t)*p, 0u);
+    if (nb == 4) {
+      const u32x2 v = ld_stream<u32x2>(p);
+      return make_uint2(v.x, v.y);
+    }
+    if (nb == 2) return make_uint2(ld_stream<uint32_t>(p), 0u);
+    return make_uint2((uint32_t)ld_stream<uint16_t>(p), 0u);
   };
   // lim: last valid in-tile position (0 for the dummy prefetch after the
   // last tile, which then reads one line per chunk, an L2 hit)
@@ -213,18 +217,18 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     for (int k = 0; k < NCV; ++k) {
       const uint8_t *p = tile + (unsigned)(k * (TILE * CV) + tok * CV);
       if constexpr (CV == 16) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(p);
+        const u32x4 x = ld_stream<u32x4>(p);
         vw[4 * k] = x.x; vw[4 * k + 1] = x.y; vw[4 * k + 2] = x.z; vw[4 * k + 3] = x.w;
       } else if constexpr (CV == 8) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(p);
+        const u32x2 x = ld_stream<u32x2>(p);
         vw[2 * k] = x.x; vw[2 * k + 1] = x.y;
       } else if constexpr (CV == 4) {
-        vw[k] = *reinterpret_cast<const uint32_t *>(p);
+        vw[k] = ld_stream<uint32_t>(p);
       } else if constexpr (CV == 2) {
-        const uint32_t x = *reinterpret_cast<const uint16_t *>(p);
+        const uint32_t x = ld_stream<uint16_t>(p);
         if (k & 1) vw[k / 2] |= x << 16; else vw[k / 2] = x;
       } else {
-        const uint32_t x = *p;
+        const uint32_t x = ld_stream<uint8_t>(p);
         if (k & 3) vw[k / 4] |= x << (8 * (k & 3)); else vw[k / 4] = x;
       }
     }

@@ -19,21 +19,26 @@ struct DecodePlan {
   bool qsum;                      // per-block query sums needed (_1 keys)
 };
 
+// Kernel arguments of the split-K decode.  The scalars and pointers every
+// workgroup reads before its first load come first, so they share the first
+// lines of the argument buffer; the plane descriptions (with the low-rank
+// tables) follow.
 struct DecodeArgs {
-  PlaneArgs k, v;
+  int S_tail, S_body, S_total;    // context splits per (b, kv head, head group)
+  int NHG, HG, G;                 // head groups per kv head, heads per group, GQA group
+  int B, Hkv, Hq;
+  int body_tokens, tail_tokens;
+  int tps_body, tps_tail;         // 64-token tiles per split
+  int tt_body;
+  float scale_body;               // multiplier taking body scores to the log2 domain
+  float scale_tail;
   const float *q_body;    // [B][Hq][128] (raw query, or pre-transformed)
   const float *q_tail;    // [B][Hq][128] raw query
   const float *qsum;      // [B][Hq][4] per-block query sums (_1 keys)
-  float scale_body;       // multiplier taking body scores to the log2 domain
-  float scale_tail;
   float *part;            // [B][Hq][S_total][PSTRIDE]
   float *out;             // [B][Hq][128] final output
   unsigned *cnt;          // [B][Hkv][NHG] finished-split counters (zero between calls)
-  int B, Hkv, Hq, G, HG, NHG;
-  int body_tokens, tail_tokens;
-  int S_body, S_tail, S_total;
-  int tps_body, tps_tail;
-  int tt_body;
+  PlaneArgs k, v;
 };
 
 hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
