@@ -757,7 +757,7 @@ struct BodyLds<C, true> {
 // LR: per-head widths and codecs (low-rank planes, offsets from the head
 // tables); otherwise every plane has the configuration's fixed geometry.
 template <class C, bool LR>
-__device__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
+__device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
   long long kco, kso, vco, vso;
   if constexpr (LR) {
     const HeadGeom gk = head_geom(a.k, b, kvh), gv = head_geom(a.v, b, kvh);
@@ -788,7 +788,7 @@ __device__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uin
 }
 
 template <int HG>
-__device__ void run_tail(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
+__device__ __forceinline__ void run_tail(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
   using C = Cfg<HG, KVQ_F16, KVQ_F16, D, D>;
   const long long plane = (long long)b * a.Hkv + kvh;
   const int head0 = kvh * a.G + hg * HG;

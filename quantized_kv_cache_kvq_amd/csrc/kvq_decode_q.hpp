@@ -35,6 +35,17 @@ __host__ __device__ constexpr int grp8_perm(int e) {
        : e;
 }
 
+// Four B-bit codes (LSB first in the low 4*B bits of v; higher bits are
+// ignored) spread to the four bytes of a word, code i in byte i: codes 2, 3
+// move up to bit 16, then codes 1, 3 up by 8 - B.
+template <int B>
+__device__ __forceinline__ uint32_t spread4(uint32_t v) {
+  constexpr uint32_t m2 = (1u << (2 * B)) - 1u;
+  const uint32_t t = (v & m2) | ((v & (m2 << (2 * B))) << (16 - 2 * B));
+  constexpr uint32_t m1 = ((1u << B) - 1u) * 0x10001u;
+  return (t & m1) | ((t & (m1 << B)) << (8 - B));
+}
+
 // 8 codes of one group (LSB first in the low 8*B bits of w) as offset-binary
 // bytes u (u = c + 2^(B-1) for _0 codes, u = c for _1 codes); byte e holds
 // channel grp8_perm<B>(e).  8-bit codes are returned as stored.
@@ -54,17 +65,15 @@ __device__ __forceinline__ uint2 group_bytes(uint64_t w) {
     return make_uint2(__umul24(x & 0xFu, 0x00204081u) & 0x01010101u,
                       __umul24(x >> 4, 0x00204081u) & 0x01010101u);
   } else {
-    constexpr uint64_t m = (1u << B) - 1u;
+    // 3, 5, 6 bits: codes 0-3 and 4-7 spread separately (bits of w above
+    // 8*B are ignored)
     uint64_t sgn = 0;
     if constexpr (FAM == FAM_0) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) sgn |= (uint64_t)1 << (B * i + B - 1);
     }
     const uint64_t x = w ^ sgn;
-    uint32_t o[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i >> 2] |= (uint32_t)((x >> (B * i)) & m) << (8 * (i & 3));
-    return make_uint2(o[0], o[1]);
+    return make_uint2(spread4<B>((uint32_t)x), spread4<B>((uint32_t)(x >> (4 * B))));
   }
 }
 
@@ -129,6 +138,16 @@ __device__ __forceinline__ uint64_t kq_load(const uint8_t *__restrict__ tile, in
     } else {
       return ld_stream<uint8_t>(p);
     }
+  } else if constexpr (CK >= 4) {
+    // the two aligned words around the group's B bytes (a word never
+    // straddles a chunk; the second is clamped into the row when the group
+    // ends inside the first), then a byte funnel shift
+    const int q0 = b0 & ~3, sh = b0 & 3;
+    const int q1 = q0 + 4 < Q::RK ? q0 + 4 : Q::RK - 4;
+    const uint32_t d0 = ld_stream<uint32_t>(tile + (unsigned)((q0 / CK) * (TILE * CK) + tok * CK + q0 % CK));
+    const uint32_t d1 = ld_stream<uint32_t>(tile + (unsigned)((q1 / CK) * (TILE * CK) + tok * CK + q1 % CK));
+    const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, (uint32_t)sh);
+    return (uint64_t)lo | ((uint64_t)(d1 >> (8 * sh)) << 32);
   } else {
     uint64_t w = 0;
 #pragma unroll
