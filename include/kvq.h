@@ -143,6 +143,20 @@ kvq_status kvq_plane_bytes(const kvq_layer *layer, int32_t which, size_t *codes_
 kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const float *v_new,
                                int32_t n_new, void *stream);
 
+/* Read back plane `which` (0 = K, 1 = V) as the binary32 vectors decode
+ * attention attends over, in the raw (input) basis:
+ * out[b][t][h][0..127] for t < n_tokens, float32 [batch][n_tokens][n_kv_heads]
+ * [128] in device memory (caller-owned, written whole).  The newest
+ * min(tail_len, n_tokens) tokens are their binary16 tail-ring copies
+ * (release notes, precision-tail section); the others are decoded rows (q*d,
+ * fma(u, d, m), or the binary16 value) taken back to the raw basis: KVarN
+ * x = (H y / 128) / w (release notes, KVarN section; H H = 128 I), low rank
+ * x = P_h u (KV-COBRA explainer; coordinates past rank_h are zero).
+ * Decode's output equals plain softmax attention over these K and V up to
+ * rounding.  n_tokens == 0 writes nothing.  A read-back and measurement
+ * path, not tuned for speed. */
+kvq_status kvq_dequantize(const kvq_layer *layer, int32_t which, float *out, void *stream);
+
 /* Re-encode the body rows [0, n_tokens) of K and V from src's codecs to
  * dst's codecs in the same basis (VBR degrade step), out of place: dst's
  * codes/scales/mins are written, src is only read, the tails are untouched

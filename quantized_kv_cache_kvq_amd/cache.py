@@ -127,6 +127,17 @@ class LayerCache:
                              ws.numel(), _stream(self.device, stream), body_splits)
         return out
 
+    def dequantize(self, which, out=None, stream=None):
+        """The K (which="k") or V ("v") vectors decode attends over, raw
+        basis: float32 [B, n_tokens, Hkv, 128] on the device."""
+        shape = (self.batch, self.n_tokens, self.n_kv_heads, lib.HEAD_DIM)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be contiguous float32 %s" % (shape,))
+        lib.dequantize(self.desc, {"k": 0, "v": 1}[which], _ptr(out), _stream(self.device, stream))
+        return out
+
     def transcode(self, kcodec, vcodec, stream=None):
         """A new layer with K and V re-encoded; shares this layer's tails."""
         ks = PlaneSpec(kcodec, self.kspec.basis, self.kspec.w)

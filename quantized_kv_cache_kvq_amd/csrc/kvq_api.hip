@@ -270,6 +270,23 @@ kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const
   return ok();
 }
 
+kvq_status kvq_dequantize(const kvq_layer *layer, int32_t which, float *out, void *stream) {
+  kvq_status s = check_layer(layer);
+  if (s != KVQ_OK) return s;
+  if (which != 0 && which != 1) return fail(KVQ_ERR_INVALID_ARG, "which must be 0 (K) or 1 (V)");
+  if (layer->n_tokens == 0) return ok();
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out is NULL");
+  if ((long long)layer->batch * layer->n_kv_heads > 65535LL * 65535LL || layer->batch > 65535 ||
+      layer->n_kv_heads > 65535)
+    return fail(KVQ_ERR_UNSUPPORTED, "batch or n_kv_heads above 65535");
+  const PlaneArgs p = plane_args(*layer, which ? layer->v : layer->k);
+  const int n_tail = layer->tail_len < layer->n_tokens ? layer->tail_len : layer->n_tokens;
+  hipError_t e = launch_dequant(p, layer->batch, layer->n_tokens, n_tail, out,
+                                reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return ok();
+}
+
 kvq_status kvq_transcode_layer(const kvq_layer *src, const kvq_layer *dst, void *stream) {
   kvq_status s = check_layer(src);
   if (s != KVQ_OK) return s;

@@ -44,6 +44,11 @@ struct DecodeArgs {
 hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
                          const float *v_new, int batch, int n_new, int t0, hipStream_t stream);
 
+// Raw-basis binary32 view of plane p, out[B][T][hkv][128]; the newest
+// n_tail tokens come from the tail ring.
+hipError_t launch_dequant(const PlaneArgs &p, int batch, int T, int n_tail, float *out,
+                          hipStream_t stream);
+
 hipError_t launch_transcode(const PlaneArgs &src, const PlaneArgs &dst, int batch, int T,
                             hipStream_t stream);
 

@@ -70,6 +70,8 @@ _SIGS = {
                                            ctypes.c_int32, ctypes.c_void_p]),
     "kvq_transcode_layer": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.POINTER(kvq_layer),
                                            ctypes.c_void_p]),
+    "kvq_dequantize": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
     "kvq_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kvq_layer), ctypes.c_int32]),
     "kvq_decode_attention": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
@@ -141,6 +143,10 @@ def quantize_append(layer, k_new_ptr, v_new_ptr, n_new, stream):
 
 def transcode_layer(src, dst, stream):
     check(load().kvq_transcode_layer(ctypes.byref(src), ctypes.byref(dst), stream))
+
+
+def dequantize(layer, which, out_ptr, stream):
+    check(load().kvq_dequantize(ctypes.byref(layer), which, out_ptr, stream))
 
 
 def decode_workspace_bytes(layer, n_q_heads):
