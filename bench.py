@@ -307,6 +307,28 @@ def transcode_rate(wl, ks, vs, capacity, k, v, plane_out, n, dev, stream):
             "frac_of_hbm_peak": round(tr_gbs / HBM_PEAK_GBS, 4)}
 
 
+def quality(args, dev):
+    """Quality sweep (codec x tail x plain/KVarN) on the rotated-3-bit
+    workload's key and value statistics (Student-t keys with outlier
+    channels, normal values) at one batch entry, 8 kv heads, 32 query heads
+    and the given context; queries attend to a few recent and a few older
+    tokens.  Prints one JSON line per configuration, then a summary line."""
+    from quantized_kv_cache_kvq_amd import quality as Q
+    wl = synth.WORKLOADS["kvarn_q3_tail2048"].with_(B=1, Hq=32, T=args.quality_tokens)
+    k = synth.layer_rows(wl, 0, "k", device=dev)
+    v = synth.layer_rows(wl, 0, "v", device=dev)
+    q_all = synth.peaked_queries(wl, k, args.quality_queries, device=dev)
+    ent, ent_max = Q.entropy_nats(q_all, k, wl.sm_scale)
+    print(json.dumps({"quality_setup": {"T": wl.T, "Hkv": wl.Hkv, "Hq": wl.Hq,
+                                        "queries": args.quality_queries,
+                                        "median_attention_entropy_nats": round(ent, 3),
+                                        "uniform_entropy_nats": round(ent_max, 3)}}), flush=True)
+    t0 = time.time()
+    rows = Q.sweep(k, v, q_all, wl.sm_scale,
+                   log=lambda r: print(json.dumps(r), flush=True))
+    print(json.dumps({"quality_rows": len(rows), "seconds": round(time.time() - t0, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +339,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", action="store_true",
                     help="measure prefill-scale append and layer transcode instead")
+    ap.add_argument("--quality", action="store_true",
+                    help="run the quality sweep (codec x tail x basis) instead")
+    ap.add_argument("--quality-tokens", type=int, default=65536)
+    ap.add_argument("--quality-queries", type=int, default=4)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -332,6 +358,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.prefill:
         prefill(args, dev)
+        return
+    if args.quality:
+        quality(args, dev)
         return
     wl = synth.WORKLOADS[args.workload]
     if wl.name == "tiny":

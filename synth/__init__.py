@@ -185,3 +185,36 @@ def kvarn_normalizers(wl, layer, which, calib_tokens=4096):
         sigma = x.std(dim=0, unbiased=False)
         w[h] = (1.0 / sigma).to(torch.float32)
     return w
+
+
+def peaked_queries(wl, k, n, device="cpu", layer=0, recent=1024, targets=(6, 2), strength=9.0,
+                   step=0):
+    """Queries that attend to a few tokens (the quality sweep's stand-in for a
+    model's attention).  For each (query, batch entry, query head), `targets`
+    = (a, b) tokens are drawn among the newest `recent` and among the older
+    ones; with s the channel scales of the kv head's keys and z_j = k_j / s,
+    q = strength * sqrt(128) * sum_j (z_j / s) / |z_j|^2 + N(0, 1) / sqrt(128):
+    a target's own term in q . k_j / sqrt(128) is `strength`, and the
+    channels the scales blow up (outliers) weigh no more than the others.
+    k: [B, T, Hkv, 128] (the keys, on `device`).  Returns [n, B, Hq, 128]."""
+    B, T, Hkv, _ = k.shape
+    G = wl.Hq // Hkv
+    g = _gen("cpu", wl.seed, "peaked", step)
+    out = torch.empty((n, B, wl.Hq, D), dtype=torch.float32, device=device)
+    scales = [channel_scales(wl, layer, "k", h).to(device) for h in range(Hkv)]
+    a, b = targets
+    lo = max(0, T - recent)
+    for i in range(n):
+        for bb in range(B):
+            for hq in range(wl.Hq):
+                idx = []
+                if T - lo > 0 and a > 0:
+                    idx += (lo + torch.randint(0, T - lo, (a,), generator=g)).tolist()
+                if lo > 0 and b > 0:
+                    idx += torch.randint(0, lo, (b,), generator=g).tolist()
+                s = scales[hq // G]
+                z = k[bb, idx, hq // G, :].double() / s
+                dirs = (z / s) / (z * z).sum(-1, keepdim=True)
+                noise = torch.randn((D,), generator=g, dtype=torch.float64).to(device) * INV_SQRT_D
+                out[i, bb, hq] = (strength * math.sqrt(D) * dirs.sum(0) + noise).to(torch.float32)
+    return out
