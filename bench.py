@@ -88,7 +88,7 @@ def build_layer(wl, layer, codec, dev, capacity):
 
 def clone_layer(src):
     dst = LayerCache(src.batch, src.n_kv_heads, src.capacity, src.tail_len, src.kspec,
-                     src.vspec, src.device)
+                     src.vspec, src.device, tail_format=src.tail_format)
     for name in ("k", "v"):
         for key, t in src.bufs[name].items():
             if t is not None:
@@ -380,7 +380,7 @@ def main():
         s = reps[0][src]
         transcode_dst = (src, LayerCache(s.batch, s.n_kv_heads, s.capacity, s.tail_len,
                                          PlaneSpec("q8_0"), PlaneSpec("q8_0"), dev,
-                                         share_tail_with=s))
+                                         share_tail_with=s, tail_format=s.tail_format))
     stream = torch.cuda.current_stream(dev)
 
     def step(i):

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_HEAD_DIM 128        /* the only supported head_dim */
 #define KVQ_TILE_TOKENS 64      /* capacity and tail_len are multiples of this */
 #define KVQ_MAX_LOWRANK_HEADS 32
@@ -99,9 +99,9 @@ typedef enum kvq_basis {
  *  - scales / mins: binary16 bit patterns, per plane [C][n/L] token-major
  *    (L = 32, or min(32, rank_h)); mins only for _1 codecs (NULL otherwise);
  *    both NULL for KVQ_F16.
- *  - tail: binary16 rows of the raw (unrotated, unprojected) vectors,
- *    [B][Hkv] planes of tail_len rows in the same 64-token tiled layout
- *    (R = 256).  NULL when tail_len == 0.
+ *  - tail: 16-bit rows (binary16 or bfloat16, kvq_layer.tail_format) of the
+ *    raw (unrotated, unprojected) vectors, [B][Hkv] planes of tail_len rows
+ *    in the same 64-token tiled layout (R = 256).  NULL when tail_len == 0.
  * Sizes: kvq_plane_bytes.
  */
 typedef struct kvq_plane {
@@ -119,6 +119,14 @@ typedef struct kvq_plane {
                                    (_0 or _1; not F16) */
 } kvq_plane;
 
+/* Element type of the precision-tail rows (release notes, precision-tail
+ * section: the newest tokens are kept in BF16 or F16).  Both K and V tails of
+ * a layer use it.  Conversions from binary32 round to nearest, ties to even. */
+typedef enum kvq_tail_format {
+    KVQ_TAIL_F16 = 0,           /* binary16 */
+    KVQ_TAIL_BF16 = 1           /* bfloat16 (binary32 with 16 low bits dropped) */
+} kvq_tail_format;
+
 typedef struct kvq_layer {
     kvq_plane k, v;
     int32_t batch;              /* B >= 1 */
@@ -127,6 +135,7 @@ typedef struct kvq_layer {
     int32_t capacity;           /* rows per plane, multiple of 64 */
     int32_t tail_len;           /* N, multiple of 64, 0 = no tail */
     int32_t n_tokens;           /* T tokens already cached, 0 <= T <= capacity */
+    int32_t tail_format;        /* kvq_tail_format of both tails */
 } kvq_layer;
 
 /* Byte sizes of the device buffers of K (which = 0) or V (which = 1):

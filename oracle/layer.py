@@ -28,7 +28,7 @@ import numpy as np
 from . import attention, cobra, kvarn
 from .codecs import CODECS, decode_rows, encode_rows
 from .layout import pack_rows, row_bytes, tile_plane, unpack_rows, untile_plane
-from .rounding import f16_bits, f16_from_bits, rn16
+from .rounding import bf16_bits, f16_bits, f16_from_bits, rbf16, rn16
 
 D = 128
 
@@ -95,16 +95,18 @@ def dequant_head(enc, spec, h, exact=True):
     return to_raw(vals, spec, h)
 
 
-def tail_ring(x, N):
+def tail_ring(x, N, fmt="f16"):
     """The tail ring after appending tokens 0..T-1 of x: [B, T, Hkv, 128].
 
-    Returns binary16 [B, Hkv, N, 128]; slots never written hold zeros.
+    Returns [B, Hkv, N, 128]: binary16 values (fmt "f16"), or bfloat16 values
+    held as float32 (fmt "bf16"); slots never written hold zeros.
     """
     x = np.asarray(x)
     B, T, Hkv, _ = x.shape
-    ring = np.zeros((B, Hkv, N, D), dtype=np.float16)
+    rnd = {"f16": rn16, "bf16": lambda y: rbf16(y).astype(np.float32)}[fmt]
+    ring = np.zeros((B, Hkv, N, D), dtype=np.float16 if fmt == "f16" else np.float32)
     for t in range(T):
-        ring[:, :, t % N, :] = rn16(x[:, t, :, :])
+        ring[:, :, t % N, :] = rnd(x[:, t, :, :])
     return ring
 
 
@@ -209,13 +211,18 @@ def unpack_plane(buf, spec, B, Hkv, capacity, T):
     return out
 
 
-def pack_tail(ring):
-    """Device bytes of a tail ring binary16 [B, Hkv, N, 128]: F16 planes."""
+def pack_tail(ring, fmt="f16"):
+    """Device bytes of a tail ring [B, Hkv, N, 128] (``tail_ring``'s output):
+    256-byte rows of 16-bit values in the tiled layout."""
     B, Hkv, N, _ = ring.shape
     planes = []
     for b in range(B):
         for h in range(Hkv):
-            rows = pack_rows({"values": ring[b, h]}, "f16")
+            if fmt == "f16":
+                rows = pack_rows({"values": ring[b, h]}, "f16")
+            else:
+                bits = np.ascontiguousarray(bf16_bits(ring[b, h]))
+                rows = bits.view(np.uint8).reshape(N, 2 * D)
             planes.append(tile_plane(rows))
     return np.concatenate(planes) if planes else np.zeros(0, np.uint8)
 

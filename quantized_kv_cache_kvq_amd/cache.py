@@ -38,7 +38,7 @@ def _ptr(t):
 
 class LayerCache:
     def __init__(self, batch, n_kv_heads, capacity, tail_len, kspec: PlaneSpec,
-                 vspec: PlaneSpec, device="cuda", share_tail_with=None):
+                 vspec: PlaneSpec, device="cuda", share_tail_with=None, tail_format="f16"):
         self.device = torch.device(device)
         self.batch, self.n_kv_heads = batch, n_kv_heads
         self.capacity, self.tail_len = capacity, tail_len
@@ -47,6 +47,10 @@ class LayerCache:
         self.desc.batch, self.desc.n_kv_heads = batch, n_kv_heads
         self.desc.head_dim, self.desc.capacity = lib.HEAD_DIM, capacity
         self.desc.tail_len, self.desc.n_tokens = tail_len, 0
+        if tail_format not in lib.TAIL_FORMATS:
+            raise ValueError("tail_format must be one of %s" % (lib.TAIL_FORMATS,))
+        self.tail_format = tail_format
+        self.desc.tail_format = lib.TAIL_FORMATS.index(tail_format)
         self._keep = []
         self.bufs = {}
         for which, name, spec in ((0, "k", kspec), (1, "v", vspec)):
@@ -143,7 +147,7 @@ class LayerCache:
         ks = PlaneSpec(kcodec, self.kspec.basis, self.kspec.w)
         vs = PlaneSpec(vcodec, self.vspec.basis, self.vspec.w)
         dst = LayerCache(self.batch, self.n_kv_heads, self.capacity, self.tail_len, ks, vs,
-                         self.device, share_tail_with=self)
+                         self.device, share_tail_with=self, tail_format=self.tail_format)
         dst.n_tokens = self.n_tokens
         lib.transcode_layer(self.desc, dst.desc, _stream(self.device, stream))
         return dst

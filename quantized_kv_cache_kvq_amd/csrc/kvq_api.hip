@@ -82,6 +82,8 @@ kvq_status check_layer(const kvq_layer *L) {
   if (L->tail_len < 0 || L->tail_len % KVQ_TILE_TOKENS)
     return fail(KVQ_ERR_INVALID_ARG, "tail_len %d must be a non-negative multiple of %d",
                 L->tail_len, KVQ_TILE_TOKENS);
+  if (L->tail_format != KVQ_TAIL_F16 && L->tail_format != KVQ_TAIL_BF16)
+    return fail(KVQ_ERR_INVALID_ARG, "tail_format %d is not a kvq_tail_format", L->tail_format);
   if (L->n_tokens < 0 || L->n_tokens > L->capacity)
     return fail(KVQ_ERR_INVALID_ARG, "n_tokens %d outside [0, capacity %d]", L->n_tokens, L->capacity);
   kvq_status s = check_plane(*L, L->k, "k");
@@ -112,6 +114,7 @@ PlaneArgs plane_args(const kvq_layer &L, const kvq_plane &p) {
   a.hkv = L.n_kv_heads;
   a.capacity = L.capacity;
   a.tail_len = L.tail_len;
+  a.tail_bf16 = L.tail_format == KVQ_TAIL_BF16;
   if (p.basis == KVQ_BASIS_LOWRANK) {
     for (int h = 0; h < L.n_kv_heads; ++h) {
       a.hcodec[h] = (int8_t)p.head_codec[h];
@@ -294,7 +297,7 @@ kvq_status kvq_transcode_layer(const kvq_layer *src, const kvq_layer *dst, void 
   if (s != KVQ_OK) return s;
   if (src->batch != dst->batch || src->n_kv_heads != dst->n_kv_heads ||
       src->capacity != dst->capacity || src->tail_len != dst->tail_len ||
-      src->n_tokens != dst->n_tokens)
+      src->n_tokens != dst->n_tokens || src->tail_format != dst->tail_format)
     return fail(KVQ_ERR_INVALID_ARG, "src and dst layers differ in shape or n_tokens");
   if (src->k.basis != dst->k.basis || src->v.basis != dst->v.basis)
     return fail(KVQ_ERR_INVALID_ARG, "transcode keeps the basis: src and dst bases differ");

@@ -1,12 +1,13 @@
 // Append kernel: rotate / project, block-quantise, bit-pack and store new
-// tokens, plus their binary16 precision-tail copy.
+// tokens, plus their 16-bit precision-tail copy.
 //
 // One wave (64 lanes) per item = (batch entry, new token, kv head, K|V);
 // 4-wave workgroups stride over the items.  Lane l owns raw channels 2l,
 // 2l+1.  Steps, after the BeeLlama v0.4.0 notes (KVarN and precision-tail
 // sections) and the KV-COBRA explainer (projection with the Hadamard
 // rotation fused in):
-//   1. tail copy: RN16 of the raw vector into ring slot t mod tail_len;
+//   1. tail copy: the raw vector rounded to the tail format (binary16 or
+//      bfloat16) into ring slot t mod tail_len;
 //   2. stored coordinates: x (plain), H (x * w) by an in-wave fast
 //      Walsh-Hadamard transform (hadamard), or P_h^T x (low rank);
 //   3. per 32-block (or min(32, rank) block) scale (and min);
@@ -93,13 +94,16 @@ __device__ void append_item(const PlaneArgs &kp, const PlaneArgs &vp, int n_new,
   const int lane = threadIdx.x & 63;
 
 
-  // 1. precision tail: binary16 raw copy, slot t mod N, 256-byte rows.  Only
+  // 1. precision tail: 16-bit raw copy (binary16 or bfloat16), slot t mod N,
+  //    256-byte rows.  Only
   //    the newest N tokens of this call write: older ones in the same call
   //    would race for the slots they share with newer ones.
   if (p.tail_len > 0 && i + p.tail_len >= n_new) {
     const long long plane = (long long)b * hkv + h;
     const int slot = t % p.tail_len;
-    uint32_t pair = (uint32_t)f32_to_f16_bits(x.x) | ((uint32_t)f32_to_f16_bits(x.y) << 16);
+    const uint32_t pair =
+        p.tail_bf16 ? (uint32_t)f32_to_bf16_bits(x.x) | ((uint32_t)f32_to_bf16_bits(x.y) << 16)
+                    : (uint32_t)f32_to_f16_bits(x.x) | ((uint32_t)f32_to_f16_bits(x.y) << 16);
     uint8_t *base = reinterpret_cast<uint8_t *>(p.tail) + plane * p.tail_len * (2 * D);
     const int byte = 4 * lane;
     *reinterpret_cast<uint32_t *>(base + tiled_offset(slot, byte / 16, 2 * D, 16) + byte % 16) = pair;

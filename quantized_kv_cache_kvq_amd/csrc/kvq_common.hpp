@@ -64,6 +64,7 @@ struct PlaneArgs {
   int hkv;
   int capacity;
   int tail_len;
+  int tail_bf16;      // tail rows are bfloat16 (else binary16)
   int8_t hcodec[MAXLR];   // low-rank: codec of head h
   int16_t hrank[MAXLR];   // low-rank: width of head h
 };
@@ -126,6 +127,19 @@ __device__ inline uint16_t f32_to_f16_bits(float x) {
 }
 __device__ inline float f16_bits_to_f32(uint16_t h) {
   return __half2float(__ushort_as_half(h));
+}
+
+// Binary32 <-> bfloat16: round to nearest, ties to even, on the 16 bits
+// dropped (finite inputs; a carry into the exponent is the correct result).
+__device__ inline uint16_t f32_to_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Raw-vector tail element of a plane from its 16 stored bits.
+__device__ inline float tail_to_f32(uint16_t bits, bool bf16) {
+  return bf16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
 }
 
 }  // namespace kvq

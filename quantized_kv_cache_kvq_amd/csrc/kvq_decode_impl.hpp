@@ -37,6 +37,34 @@ union H8 {
   uint32_t u[4];
 };
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 16 x 16 x 32 MFMA step on 16-bit operands: binary16, or bfloat16 (BF) with
+// the same bits carried in the half8 registers.
+template <bool BF>
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// x as a (hi, lo) pair of 16-bit values (hi = RN(x), lo = RN(x - hi)) packed
+// hi | lo << 16: binary16, or bfloat16 (BF).
+template <bool BF>
+__device__ __forceinline__ uint32_t split16(float x) {
+  if constexpr (BF) {
+    const uint16_t hi = f32_to_bf16_bits(x);
+    const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+    return (uint32_t)hi | ((uint32_t)lo << 16);
+  } else {
+    const _Float16 hi = (_Float16)x;
+    const _Float16 lo = (_Float16)(x - (float)hi);
+    return (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+  }
+}
+
 // ------------------------------------------------------------ DPP helpers --
 
 // All-reduce over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
@@ -335,7 +363,9 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(read_lane(x, 0), read_lane(x, 16)), fmaxf(read_lane(x, 32), read_lane(x, 48)));
 }
 
-template <class C>
+// BF: the binary16 rows are bfloat16 (precision tail in bfloat16); only for
+// the all-16-bit configuration.
+template <class C, bool BF = false>
 __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
   constexpr int HG = C::HG, TT = C::TT, NT = C::NT, NDT = C::NDT, NBV = C::NBV;
   constexpr int NBA = C::VFAM == FAM_F16 ? 1 : NBV;
@@ -378,11 +408,11 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
       H8 a;
       float ssum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = v[j][e] * up;
-        const _Float16 hi = (_Float16)x;
-        a.h[e] = prt ? (_Float16)(x - (float)hi) : hi;
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t p0 = split16<BF>(v[j][e] * up), p1 = split16<BF>(v[j][e + 1] * up);
+        a.u[e / 2] = prt ? (p0 >> 16) | (p1 & 0xFFFF0000u) : (p0 & 0xFFFFu) | (p1 << 16);
         ssum += v[j][e];
+        ssum += v[j][e + 1];
       }
       qa[j] = a.h;
       ssum += __shfl_xor(ssum, 16, 64);
@@ -548,7 +578,7 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
       if constexpr (C::KFAM == FAM_F16) {
         floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < C::NKB; ++j) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], kb[j], c, 0, 0, 0);
+        for (int j = 0; j < C::NKB; ++j) c = mfma16<BF>(qa[j], kb[j], c);
         a1[0] = c[0] + c[1];
         a1[1] = c[2] + c[3];
       } else {
@@ -622,12 +652,7 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
         // rows (2h, 2h+1) = (hi, lo) of head h; rows >= 2*HG stay zero
         uint32_t rw[HG];
 #pragma unroll
-        for (int h = 0; h < HG; ++h) {
-          const float x = ps[h] * scl;
-          const _Float16 hi = (_Float16)x;
-          const _Float16 lo = (_Float16)(x - (float)hi);
-          rw[h] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
-        }
+        for (int h = 0; h < HG; ++h) rw[h] = split16<BF>(ps[h] * scl);
         uint32_t *dst = reinterpret_cast<uint32_t *>(alds + ((j * TT) + tl) * 32);
         if constexpr (C::TPT == 1) {
           if constexpr (HG == 4) {
@@ -669,7 +694,7 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
             constexpr float voff = C::VFAM == FAM_0 ? (float)(1 << (C::VBITS - 1)) : 0.f;
             bv = bytes_to_half8(tr8(pb), voff);
           }
-          ct[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, ct[dt], 0, 0, 0);
+          ct[dt] = mfma16<BF>(a, bv, ct[dt]);
         }
       }
     }
@@ -787,7 +812,7 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, in
   else attend_range<C>(io, lds);
 }
 
-template <int HG>
+template <int HG, bool BF>
 __device__ __forceinline__ void run_tail(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
   using C = Cfg<HG, KVQ_F16, KVQ_F16, D, D>;
   const long long plane = (long long)b * a.Hkv + kvh;
@@ -804,7 +829,7 @@ __device__ __forceinline__ void run_tail(const DecodeArgs &a, int b, int kvh, in
   io.t_end = io.t_begin + tps < a.tail_tokens ? io.t_begin + tps : a.tail_tokens;
   io.part = a.part + (((long long)b * a.Hq + head0) * a.S_total + s) * PSTRIDE;
   io.part_head_stride = (long long)a.S_total * PSTRIDE;
-  attend_range<C>(io, lds);
+  attend_range<C, BF>(io, lds);
 }
 
 // ------------------------------------------------------ split combine ----
@@ -963,7 +988,7 @@ __device__ __forceinline__ void fetch_args(const DecodeArgs &a) {
                "s"(a.q_tail), "s"(a.part));
   asm volatile("" ::"s"(a.k.codes), "s"(a.k.scales), "s"(a.k.mins), "s"(a.k.tail),
                "s"(a.k.capacity), "s"(a.k.tail_len), "s"(a.v.codes), "s"(a.v.scales),
-               "s"(a.v.mins), "s"(a.v.tail));
+               "s"(a.v.mins), "s"(a.v.tail), "s"(a.k.tail_bf16));
 }
 
 template <int HG, int KC, int VC>
@@ -973,7 +998,10 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax<BodyLds<CB>::bytes, CT::LDS_BYTES>::value];
   int b, kvh, hg, s;
   fetch_args(a);
-  if (split_decode(a, b, kvh, hg, s)) run_tail<HG>(a, b, kvh, hg, s, lds);
+  if (split_decode(a, b, kvh, hg, s)) {
+    if (a.k.tail_bf16) run_tail<HG, true>(a, b, kvh, hg, s, lds);
+    else run_tail<HG, false>(a, b, kvh, hg, s, lds);
+  }
   else run_body<CB, false>(a, b, kvh, hg, s, lds);
   finish_split(a, b, kvh, hg, lds);
 }
@@ -999,7 +1027,8 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(De
   int b, kvh, hg, s;
   fetch_args(a);
   if (split_decode(a, b, kvh, hg, s)) {
-    run_tail<HG>(a, b, kvh, hg, s, lds);
+    if (a.k.tail_bf16) run_tail<HG, true>(a, b, kvh, hg, s, lds);
+    else run_tail<HG, false>(a, b, kvh, hg, s, lds);
   } else {
     const int codec = a.k.hcodec[kvh], rank = a.k.hrank[kvh];
 #define KVQ_LR_DISPATCH(CC, RR)                                                           \

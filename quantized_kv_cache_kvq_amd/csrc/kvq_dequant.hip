@@ -2,7 +2,7 @@
 // in the raw (input) basis, for every stored token of every (batch, kv head).
 //
 // A reader of the cache sees, for token t of n tokens:
-//  - the binary16 tail ring slot t mod tail_len when t is one of the newest
+//  - the 16-bit tail ring slot t mod tail_len when t is one of the newest
 //    min(tail_len, n) tokens (BeeLlama.cpp v0.4.0 release notes, precision
 //    tail section);
 //  - otherwise the block-coded row decoded (q*d for _0, fma(u, d, m) for _1,
@@ -47,14 +47,14 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void dequant_kernel(PlaneArgs p, int
   if (t >= T) return;
   float x0 = 0.f, x1 = 0.f;
   if (t >= T - n_tail) {
-    // binary16 ring row: 256-byte rows in the tiled layout (16-byte chunks)
+    // 16-bit ring row: 256-byte rows in the tiled layout (16-byte chunks)
     const long long plane = (long long)b * p.hkv + h;
     const uint8_t *ring = reinterpret_cast<const uint8_t *>(p.tail) + plane * p.tail_len * (2 * D);
     const int slot = t % p.tail_len, byte = 4 * lane;
     const uint32_t w =
         *reinterpret_cast<const uint32_t *>(ring + tiled_offset(slot, byte / 16, 2 * D, 16) + byte % 16);
-    x0 = f16_bits_to_f32((uint16_t)(w & 0xFFFF));
-    x1 = f16_bits_to_f32((uint16_t)(w >> 16));
+    x0 = tail_to_f32((uint16_t)(w & 0xFFFF), p.tail_bf16);
+    x1 = tail_to_f32((uint16_t)(w >> 16), p.tail_bf16);
   } else {
     const HeadGeom g = head_geom(p, b, h);
     const int fam = codec_family(g.codec), bits = codec_bits(g.codec);

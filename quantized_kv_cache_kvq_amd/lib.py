@@ -48,7 +48,11 @@ class kvq_layer(ctypes.Structure):
         ("capacity", ctypes.c_int32),
         ("tail_len", ctypes.c_int32),
         ("n_tokens", ctypes.c_int32),
+        ("tail_format", ctypes.c_int32),
     ]
+
+
+TAIL_FORMATS = ("f16", "bf16")       # kvq_tail_format order
 
 
 class KvqError(RuntimeError):
@@ -110,7 +114,7 @@ def load(path=LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.kvq_abi_version() != 1:
+    if lib.kvq_abi_version() != 2:
         raise RuntimeError("libkvq.so ABI version mismatch")
     _lib = lib
     return lib

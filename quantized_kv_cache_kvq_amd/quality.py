@@ -8,6 +8,8 @@ tails 0, 1024 and 2048, 64k context) without a model: the divergence here is
 between one query's attention weights over exact and over packed keys, not
 between a model's output distributions, so only the trends compare.
 
+Tails are binary16 or bfloat16 (the release notes allow either).
+
 Per configuration, on the device: the layer is built by the library's append
 (one call over the whole context), the outputs come from the library's
 decode, and the keys attended over are the library's read-back
@@ -72,9 +74,10 @@ def measure(layer, q_all, K, V, sm_scale):
 
 
 def sweep(k, v, q_all, sm_scale, codecs=CODECS, tails=TAILS, bases=BASES, calib_tokens=4096,
-          log=None):
+          tail_formats=("f16", "bf16"), log=None):
     """k, v: [B, T, Hkv, 128] float32 on the device; q_all [n, B, Hq, 128].
-    Returns one dict per (basis, codec, tail)."""
+    Returns one dict per (basis, codec, tail, tail format); tail 0 has one
+    row (format "-")."""
     B, T, Hkv, _ = k.shape
     capacity = (T + 63) // 64 * 64
     K, V = k.double(), v.double()
@@ -85,16 +88,18 @@ def sweep(k, v, q_all, sm_scale, codecs=CODECS, tails=TAILS, bases=BASES, calib_
     for basis in bases:
         for codec in codecs:
             for tail in tails:
-                ks = PlaneSpec(codec, basis, w["k"] if basis == "hadamard" else None)
-                vs = PlaneSpec(codec, basis, w["v"] if basis == "hadamard" else None)
-                layer = LayerCache(B, Hkv, capacity, tail, ks, vs, k.device)
-                layer.append(k, v)
-                r = {"basis": basis, "codec": codec, "bits": bits_per_value(codec), "tail": tail}
-                r.update(measure(layer, q_all, K, V, sm_scale))
-                rows.append(r)
-                if log:
-                    log(r)
-                del layer
+                for fmt in (tail_formats if tail > 0 else ("f16",)):
+                    ks = PlaneSpec(codec, basis, w["k"] if basis == "hadamard" else None)
+                    vs = PlaneSpec(codec, basis, w["v"] if basis == "hadamard" else None)
+                    layer = LayerCache(B, Hkv, capacity, tail, ks, vs, k.device, tail_format=fmt)
+                    layer.append(k, v)
+                    r = {"basis": basis, "codec": codec, "bits": bits_per_value(codec), "tail": tail,
+                         "tail_format": fmt if tail > 0 else "-"}
+                    r.update(measure(layer, q_all, K, V, sm_scale))
+                    rows.append(r)
+                    if log:
+                        log(r)
+                    del layer
     return rows
 
 

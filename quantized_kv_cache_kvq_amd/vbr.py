@@ -39,7 +39,8 @@ class VBRCache:
         for (layer, src, dst) in steps:
             old = self.layers[layer]
             new = LayerCache(old.batch, old.n_kv_heads, old.capacity, old.tail_len,
-                             PlaneSpec(dst), PlaneSpec(dst), old.device, share_tail_with=old)
+                             PlaneSpec(dst), PlaneSpec(dst), old.device, share_tail_with=old,
+                             tail_format=old.tail_format)
             old.transcode_into(new, stream=stream)
             self.layers[layer] = new
             self.history.append((n_tokens, layer, src, dst))

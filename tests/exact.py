@@ -49,3 +49,8 @@ def rn16_exact(v):
 
 def rn32_exact(v):
     return round_binary(v, 24, -126, 127)
+
+
+def rbf16_exact(v):
+    """bfloat16: 8 significand bits, binary32's exponent range."""
+    return round_binary(v, 8, -126, 127)

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
     assert len(names) >= 9
     for n in names:
         assert hasattr(L, n), n
-    assert L.kvq_abi_version() == 1
+    assert L.kvq_abi_version() == 2
     assert L.kvq_status_string(3) == b"KVQ_ERR_CAPACITY"
 
 
@@ -90,6 +90,18 @@ def test_host_validation_rejects_before_launch(L):
     assert L.kvq_quantize_append(ctypes.byref(d), 1, 1, 1, null) == lib.KVQ_ERR_INVALID_ARG
     d = _layer()
     assert L.kvq_quantize_append(ctypes.byref(d), 1, 1, 0, null) == lib.KVQ_ERR_INVALID_ARG
+    d = _layer(N=64)
+    d.tail_format = 2                                        # not a kvq_tail_format
+    assert L.kvq_quantize_append(ctypes.byref(d), 1, 1, 1, null) == lib.KVQ_ERR_INVALID_ARG
+    assert b"tail_format" in L.kvq_last_error()
+    s, dd = _layer(N=64, T=64), _layer(N=64, T=64)
+    dd.tail_format = 1                                       # transcode shares the tails
+    assert L.kvq_transcode_layer(ctypes.byref(s), ctypes.byref(dd), null) == lib.KVQ_ERR_INVALID_ARG
+    d = _layer(T=0)
+    assert L.kvq_dequantize(ctypes.byref(d), 0, null, null) == lib.KVQ_OK   # nothing to write
+    d = _layer(T=64)
+    assert L.kvq_dequantize(ctypes.byref(d), 2, 1, null) == lib.KVQ_ERR_INVALID_ARG
+    assert L.kvq_dequantize(ctypes.byref(d), 0, null, null) == lib.KVQ_ERR_INVALID_ARG
 
 
 def test_decode_validation(L):

@@ -7,10 +7,10 @@ import os
 import numpy as np
 import pytest
 
-from oracle import attention, budget, cobra, layer
+from oracle import attention, budget, cobra, layer, layout
 from oracle.codecs import encode_rows, decode_rows
 from oracle.layer import PlaneSpec
-from oracle.rounding import rn16
+from oracle.rounding import rbf16, rn16
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -116,6 +116,20 @@ def test_tail_bytes_roundtrip():
     rng = np.random.default_rng(6)
     ring = layer.tail_ring(_x(rng, 2, 300, 2), 128)
     assert np.array_equal(layer.unpack_tail(layer.pack_tail(ring), 2, 2, 128), ring)
+
+
+def test_bf16_tail_bytes():
+    """bfloat16 ring: values are the rounded inputs of the newest tokens, and
+    a row's bytes are the high halves of the values' binary32 patterns."""
+    rng = np.random.default_rng(8)
+    x = _x(rng, 1, 130, 1)
+    ring = layer.tail_ring(x, 64, fmt="bf16")
+    for t in range(66, 130):
+        assert np.array_equal(ring[0, 0, t % 64], rbf16(x[0, t, 0].astype(np.float64)).astype(np.float32))
+    raw = layer.pack_tail(ring, fmt="bf16")
+    rows = layout.untile_plane(raw, 256)
+    hi = (ring[0, 0].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(rows.view(np.uint16), hi)
 
 
 def test_cobra_worked_example():

@@ -5,8 +5,10 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle.rounding import f16_bits, f16_from_bits, rn16, rn32, rne
-from tests.exact import rn16_exact, rn32_exact, rne_int
+import torch
+
+from oracle.rounding import bf16_bits, f16_bits, f16_from_bits, rbf16, rn16, rn32, rne
+from tests.exact import rbf16_exact, rn16_exact, rn32_exact, rne_int
 
 
 def _samples(rng, n):
@@ -51,3 +53,21 @@ def test_f16_bits_roundtrip():
     x = np.array([0.0, 1.0, -2.0, 65504.0, 6.1035e-05], dtype=np.float16)
     assert list(f16_bits(x)) == [0x0000, 0x3C00, 0xC000, 0x7BFF, 0x0400]
     assert np.array_equal(f16_from_bits(f16_bits(x)), x)
+
+
+def test_rbf16_matches_exact_rational_and_torch():
+    """bfloat16 rounding (precision-tail format): exact rational rounding of
+    binary32 inputs, ties at 2^-8 spacing, subnormals; and torch's own
+    float32 -> bfloat16 conversion (round to nearest even) on many values."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(300) * np.exp(rng.uniform(-60, 60, 300))).astype(np.float32)
+    ties = np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3 * 2 ** -134, 2 ** -133,
+                       (1 + 2 ** -8) * 2 ** -100])
+    xs = np.concatenate([x, ties]).astype(np.float64)
+    got = rbf16(xs)
+    for v, g in zip(xs, got):
+        assert Fraction(float(g)) == rbf16_exact(Fraction(float(v))), (v, g)
+    assert list(got[-6:-3]) == [1.0, 1 + 2 ** -6, -1.0]
+    many = (rng.standard_normal(100000) * np.exp(rng.uniform(-80, 80, 100000))).astype(np.float32)
+    ref = torch.from_numpy(many).to(torch.bfloat16)
+    assert np.array_equal(bf16_bits(rbf16(many.astype(np.float64))), ref.view(torch.int16).numpy().view(np.uint16))
