@@ -2,7 +2,7 @@
 // tokens, plus their 16-bit precision-tail copy.
 //
 // One wave (64 lanes) per item = (batch entry, new token, kv head, K|V);
-// 4-wave workgroups stride over the items.  Lane l owns raw channels 2l,
+// 8-wave workgroups stride over the items.  Lane l owns raw channels 2l,
 // 2l+1.  Steps, after the BeeLlama v0.4.0 notes (KVarN and precision-tail
 // sections) and the KV-COBRA explainer (projection with the Hadamard
 // rotation fused in):
@@ -61,43 +61,122 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Source row of an item = (batch entry, new token, kv head, K|V).
-__device__ __forceinline__ const float *item_src(const PlaneArgs &kp, const float *__restrict__ k_new,
+// Items are plane-major, token-minor: item = ((K|V * B + b) * Hkv + h) * n_new
+// + i, so a workgroup's waves take consecutive new tokens of one plane and
+// its stores fill whole lines of the 64-token tiled layout (the chunks of
+// consecutive tokens are adjacent) inside one XCD's L2.
+struct Item {
+  int which, b, h, i;
+};
+__device__ __forceinline__ Item item_of(unsigned item, int hkv, int n_new, int batch) {
+  Item r;
+  r.i = (int)(item % (unsigned)n_new);
+  unsigned pl = item / (unsigned)n_new;
+  r.h = (int)(pl % (unsigned)hkv);
+  pl /= (unsigned)hkv;
+  r.b = (int)(pl % (unsigned)batch);
+  r.which = (int)(pl / (unsigned)batch);
+  return r;
+}
+
+// Source row of an item.
+__device__ __forceinline__ const float *item_src(const float *__restrict__ k_new,
                                                  const float *__restrict__ v_new, int n_new,
-                                                 unsigned item) {
-  unsigned id = item;
-  const int which = id & 1;
-  id >>= 1;
-  const unsigned hkv = (unsigned)kp.hkv;
-  const unsigned h = id % hkv;
-  id /= hkv;
-  const unsigned i = id % (unsigned)n_new;
-  const unsigned b = id / (unsigned)n_new;
-  return (which ? v_new : k_new) + (((long long)b * n_new + i) * hkv + h) * D;
+                                                 int hkv, const Item &it) {
+  return (it.which ? v_new : k_new) + (((long long)it.b * n_new + it.i) * hkv + it.h) * D;
+}
+
+// Per-block scale (and min), codes and bit-packed row of one token whose
+// stored coordinates are held two per lane (a = coordinate 2l, c = 2l + 1),
+// for a plain or KVarN plane of a fixed codec: blocks of 32 are the 16
+// lanes of a DPP row, so every reduction is a row reduction and nothing goes
+// through LDS except the 3/5/6-bit pack.  `rows` = rows before this
+// (b, kv head) plane.
+template <int BITS, int FAM>
+__device__ __forceinline__ void quantize_row(const PlaneArgs &p, long long rows, int t, float a, float c,
+                                             uint32_t *stage) {
+  constexpr int RB = row_bytes(FAM == FAM_0 ? KVQ_Q8_0 : KVQ_Q8_1, D) * BITS / 8;   // 16 * BITS
+  constexpr int CK = chunk_bytes(RB);
+  const int lane = threadIdx.x & 63;
+  const long long so = (rows + t) * 4 + (lane >> 4);
+  float d, m = 0.f;
+  if constexpr (FAM == FAM_0) {
+    const float amax = row_max16(fmaxf(fabsf(a), fabsf(c)));
+    constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+    const uint16_t dh = f32_to_f16_bits(amax / qmax);
+    if ((lane & 15) == 0) p.scales[so] = dh;
+    d = f16_bits_to_f32(dh);
+  } else {
+    const float lo = row_min16(fminf(a, c)), hi = row_max16(fmaxf(a, c));
+    const uint16_t mh = f32_to_f16_bits(lo);
+    m = f16_bits_to_f32(mh);
+    constexpr float levels = (float)((1 << BITS) - 1);
+    const uint16_t dh = f32_to_f16_bits((hi - m) / levels);
+    if ((lane & 15) == 0) {
+      p.scales[so] = dh;
+      p.mins[so] = mh;
+    }
+    d = f16_bits_to_f32(dh);
+  }
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  uint32_t q0 = 0, q1 = 0;
+  if (d != 0.f) {
+    if constexpr (FAM == FAM_0) {
+      constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+      q0 = (uint32_t)(int)fminf(fmaxf(rintf(a / d), -qmax), qmax);
+      q1 = (uint32_t)(int)fminf(fmaxf(rintf(c / d), -qmax), qmax);
+    } else {
+      constexpr float levels = (float)((1 << BITS) - 1);
+      q0 = (uint32_t)(int)fminf(fmaxf(rintf((a - m) / d), 0.f), levels);
+      q1 = (uint32_t)(int)fminf(fmaxf(rintf((c - m) / d), 0.f), levels);
+    }
+  }
+  // this lane's 2*BITS bits start at bit 2*BITS*lane of the row
+  const uint32_t v = (q0 & mask) | ((q1 & mask) << BITS);
+  uint8_t *tile = p.codes + rows * RB + (long long)(t / TILE) * TILE * RB;
+  const int tt = t % TILE;
+  if constexpr (BITS == 8 || BITS == 4 || BITS == 2 || BITS == 1) {
+    constexpr int K = 16 / BITS;                   // lanes per dword
+    uint32_t w = v << (2 * BITS * (lane % K));
+#pragma unroll
+    for (int o = 1; o < K; o <<= 1) w |= __shfl_xor(w, o, 64);
+    if (lane % K == 0) {
+      const int byte = 4 * (lane / K);
+      *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = w;
+    }
+  } else {
+    // 3, 5, 6 bits: OR each lane's field into the row's dwords in LDS
+    if (lane < RB / 4) stage[lane] = 0u;
+    wave_sync();
+    const int o = 2 * BITS * lane, k = o >> 5, sh = o & 31;
+    __hip_atomic_fetch_or(stage + k, v << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (sh + 2 * BITS > 32)
+      __hip_atomic_fetch_or(stage + k + 1, v >> (32 - sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    wave_sync();
+    if (lane < RB / 4) {
+      const int byte = 4 * lane;
+      *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = stage[lane];
+    }
+    wave_sync();                                   // stage is free for the next item
+  }
 }
 
 // One item, one wave; x = this lane's two raw channels (loaded by the
-// caller ahead of time).  The LDS arrays are this wave's own.
-__device__ void append_item(const PlaneArgs &kp, const PlaneArgs &vp, int n_new, int t0,
-                            unsigned item, float2 x, float *xin, float *coords, uint8_t *codes,
-                            float *s_scale, float *s_min) {
-  unsigned id = item;
-  const int which = id & 1;
-  id >>= 1;
-  const PlaneArgs &p = which ? vp : kp;
+// caller ahead of time); p is the item's plane (a kernel argument bound at
+// the call site, so its fields stay scalar loads of the argument buffer).
+// The LDS arrays are this wave's own.
+__device__ __forceinline__ void append_item(const PlaneArgs &p, int n_new, int t0, const Item &it,
+                                            float2 x, float *xin, float *coords, uint8_t *codes,
+                                            float *s_scale, float *s_min) {
   const int hkv = p.hkv;
-  const int h = (int)(id % (unsigned)hkv);
-  id /= (unsigned)hkv;
-  const int i = (int)(id % (unsigned)n_new);
-  const int b = (int)(id / (unsigned)n_new);
+  const int h = it.h, i = it.i, b = it.b;
   const int t = t0 + i;
   const int lane = threadIdx.x & 63;
 
-
   // 1. precision tail: 16-bit raw copy (binary16 or bfloat16), slot t mod N,
-  //    256-byte rows.  Only
-  //    the newest N tokens of this call write: older ones in the same call
-  //    would race for the slots they share with newer ones.
+  //    256-byte rows.  Only the newest N tokens of this call write: older
+  //    ones in the same call would race for the slots they share with newer
+  //    ones.
   if (p.tail_len > 0 && i + p.tail_len >= n_new) {
     const long long plane = (long long)b * hkv + h;
     const int slot = t % p.tail_len;
@@ -109,93 +188,64 @@ __device__ void append_item(const PlaneArgs &kp, const PlaneArgs &vp, int n_new,
     *reinterpret_cast<uint32_t *>(base + tiled_offset(slot, byte / 16, 2 * D, 16) + byte % 16) = pair;
   }
 
-  const HeadGeom g = head_geom(p, b, h);
+  // 2. plain and KVarN planes: coordinates stay in registers (the rotation
+  //    is an in-wave transform), codec fixed at compile time per case
+  if (p.basis != KVQ_BASIS_LOWRANK) {
+    float a = x.x, c = x.y;
+    if (p.basis == KVQ_BASIS_HADAMARD) {
+      const float *w = p.w + (long long)h * D;
+      a *= w[2 * lane];
+      c *= w[2 * lane + 1];
+      fwht128_wave(a, c);
+    }
+    const long long rows = ((long long)b * hkv + h) * p.capacity;
+    uint32_t *stage = reinterpret_cast<uint32_t *>(coords);
+    switch (p.codec) {
+      case KVQ_F16: {
+        // binary16 row: dword `lane` holds coordinates 2*lane, 2*lane+1
+        const uint32_t pair = (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(c) << 16);
+        const int byte = 4 * lane;
+        *reinterpret_cast<uint32_t *>(p.codes + rows * (2 * D) + tiled_offset(t, byte / 16, 2 * D, 16) +
+                                      byte % 16) = pair;
+        break;
+      }
+      case KVQ_Q8_0: quantize_row<8, FAM_0>(p, rows, t, a, c, stage); break;
+      case KVQ_Q6_0: quantize_row<6, FAM_0>(p, rows, t, a, c, stage); break;
+      case KVQ_Q5_0: quantize_row<5, FAM_0>(p, rows, t, a, c, stage); break;
+      case KVQ_Q4_0: quantize_row<4, FAM_0>(p, rows, t, a, c, stage); break;
+      case KVQ_Q3_0: quantize_row<3, FAM_0>(p, rows, t, a, c, stage); break;
+      case KVQ_Q2_0: quantize_row<2, FAM_0>(p, rows, t, a, c, stage); break;
+      case KVQ_Q8_1: quantize_row<8, FAM_1>(p, rows, t, a, c, stage); break;
+      case KVQ_Q6_1: quantize_row<6, FAM_1>(p, rows, t, a, c, stage); break;
+      case KVQ_Q5_1: quantize_row<5, FAM_1>(p, rows, t, a, c, stage); break;
+      case KVQ_Q4_1: quantize_row<4, FAM_1>(p, rows, t, a, c, stage); break;
+      case KVQ_Q3_1: quantize_row<3, FAM_1>(p, rows, t, a, c, stage); break;
+      case KVQ_Q2_1: quantize_row<2, FAM_1>(p, rows, t, a, c, stage); break;
+      case KVQ_Q1_1: quantize_row<1, FAM_1>(p, rows, t, a, c, stage); break;
+      default: break;
+    }
+    return;
+  }
 
-  // 2. stored coordinates
-  if (p.basis == KVQ_BASIS_HADAMARD) {
-    const float *w = p.w + (long long)h * D;
-    float a = x.x * w[2 * lane];
-    float c = x.y * w[2 * lane + 1];
-    fwht128_wave(a, c);
-    coords[2 * lane] = a;
-    coords[2 * lane + 1] = c;
-  } else if (p.basis == KVQ_BASIS_LOWRANK) {
-    xin[2 * lane] = x.x;
-    xin[2 * lane + 1] = x.y;
-    wave_sync();
+  // 3. low rank: u = P_h^T x through LDS, then per-head width and codec
+  const HeadGeom g = head_geom(p, b, h);
+  xin[2 * lane] = x.x;
+  xin[2 * lane + 1] = x.y;
+  wave_sync();
+  {
     const uint16_t *P = p.proj + (long long)h * D * D;
     for (int k = lane; k < g.n; k += 64) {
       float acc = 0.f;
       for (int r = 0; r < D; ++r) acc = fmaf(f16_bits_to_f32(P[r * D + k]), xin[r], acc);
       coords[k] = acc;
     }
-  } else {
-    coords[2 * lane] = x.x;
-    coords[2 * lane + 1] = x.y;
   }
   wave_sync();
 
   uint8_t *row_codes = p.codes + g.codes_off;
   const int fam = codec_family(g.codec);
-  if (fam == FAM_F16) {
-    // binary16 row: dword `lane` holds coordinates 2*lane, 2*lane+1
-    uint32_t pair = (uint32_t)f32_to_f16_bits(coords[2 * lane]) |
-                    ((uint32_t)f32_to_f16_bits(coords[2 * lane + 1]) << 16);
-    const int byte = 4 * lane;
-    *reinterpret_cast<uint32_t *>(row_codes + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c) = pair;
-    return;
-  }
-
   const int bits = codec_bits(g.codec);
-  if (p.basis != KVQ_BASIS_LOWRANK && (bits == 8 || bits == 4 || bits == 2 || bits == 1)) {
-    // 128 coordinates, lane l holds 2l and 2l+1: block j is the DPP row of
-    // lanes 16j .. 16j+15, so block statistics are row reductions; the
-    // row's bits are gathered 16/bits lanes to a dword and stored whole.
-    const float a = coords[2 * lane], c = coords[2 * lane + 1];
-    const long long so = g.scales_off + (long long)t * 4 + (lane >> 4);
-    float d, m = 0.f;
-    if (fam == FAM_0) {
-      const float amax = row_max16(fmaxf(fabsf(a), fabsf(c)));
-      const float qmax = (float)((1 << (bits - 1)) - 1);
-      const uint16_t dh = f32_to_f16_bits(amax / qmax);
-      if ((lane & 15) == 0) p.scales[so] = dh;
-      d = f16_bits_to_f32(dh);
-    } else {
-      const float lo = row_min16(fminf(a, c)), hi = row_max16(fmaxf(a, c));
-      const uint16_t mh = f32_to_f16_bits(lo);
-      m = f16_bits_to_f32(mh);
-      const float R = hi - m;
-      const float levels = (float)((1 << bits) - 1);
-      const uint16_t dh = f32_to_f16_bits(R / levels);
-      if ((lane & 15) == 0) {
-        p.scales[so] = dh;
-        p.mins[so] = mh;
-      }
-      d = f16_bits_to_f32(dh);
-    }
-    const uint32_t mask = (1u << bits) - 1u;
-    uint32_t q0 = 0, q1 = 0;
-    if (d != 0.f) {
-      if (fam == FAM_0) {
-        const float qmax = (float)((1 << (bits - 1)) - 1);
-        q0 = (uint32_t)(int)fminf(fmaxf(rintf(a / d), -qmax), qmax);
-        q1 = (uint32_t)(int)fminf(fmaxf(rintf(c / d), -qmax), qmax);
-      } else {
-        const float levels = (float)((1 << bits) - 1);
-        q0 = (uint32_t)(int)fminf(fmaxf(rintf((a - m) / d), 0.f), levels);
-        q1 = (uint32_t)(int)fminf(fmaxf(rintf((c - m) / d), 0.f), levels);
-      }
-    }
-    const int K = 16 / bits;                       // lanes per dword
-    uint32_t w = ((q0 & mask) | ((q1 & mask) << bits)) << (2 * bits * (lane % K));
-    for (int o = 1; o < K; o <<= 1) w |= __shfl_xor(w, o, 64);
-    if (lane % K == 0) {
-      const int byte = 4 * (lane / K);
-      *reinterpret_cast<uint32_t *>(row_codes + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c) = w;
-    }
-    return;
-  }
-  // 3. block scale (and min), one lane per block
+  // block scale (and min), one lane per block (blocks of min(32, rank))
   if (lane < g.nblk) {
     const float *blk = coords + lane * g.L;
     const long long so = g.scales_off + (long long)t * g.nblk + lane;
@@ -225,7 +275,7 @@ __device__ void append_item(const PlaneArgs &kp, const PlaneArgs &vp, int n_new,
   }
   wave_sync();
 
-  // 4. codes (masked to `bits` bits)
+  // codes (masked to `bits` bits)
   const uint32_t mask = (1u << bits) - 1u;
   for (int e = lane; e < g.n; e += 64) {
     const int j = e / g.L;
@@ -243,7 +293,7 @@ __device__ void append_item(const PlaneArgs &kp, const PlaneArgs &vp, int n_new,
   }
   wave_sync();
 
-  // 5. pack: unit u (us bytes) holds row bits [8*us*u, 8*us*(u+1))
+  // pack: unit u (us bytes) holds row bits [8*us*u, 8*us*(u+1))
   const int us = g.c < 4 ? g.c : 4;
   const int nunits = g.R / us;
   if (lane < nunits) {
@@ -265,31 +315,57 @@ __device__ void append_item(const PlaneArgs &kp, const PlaneArgs &vp, int n_new,
   }
 }
 
-// Items strided over a grid of 4-wave workgroups: far fewer workgroups
-// than items, so a prefill-sized append is not bound by workgroup dispatch.
-__global__ __launch_bounds__(256) void append_kernel(PlaneArgs kp, PlaneArgs vp,
-                                                     const float *__restrict__ k_new,
-                                                     const float *__restrict__ v_new, int n_new,
-                                                     int t0, unsigned items) {
-  __shared__ float xin[4][D];
-  __shared__ float coords[4][D];
-  __shared__ uint8_t codes[4][D];
-  __shared__ float s_scale[4][4];
-  __shared__ float s_min[4][4];
+// Every wave takes a contiguous run of items (consecutive new tokens of one
+// plane, moving on to the next plane at its end): the item's coordinates
+// advance by increments, with no division per item, and the next item's
+// row is loaded while the current one is processed.  8-wave workgroups;
+// far fewer workgroups than items for a prefill-sized append.
+constexpr int AP_WAVES = 8;
+
+__global__ __launch_bounds__(64 * AP_WAVES) void append_kernel(PlaneArgs kp, PlaneArgs vp,
+                                                               const float *__restrict__ k_new,
+                                                               const float *__restrict__ v_new,
+                                                               int n_new, int t0, int batch,
+                                                               unsigned items) {
+  __shared__ float xin[AP_WAVES][D];
+  __shared__ float coords[AP_WAVES][D];
+  __shared__ uint8_t codes[AP_WAVES][D];
+  __shared__ float s_scale[AP_WAVES][4];
+  __shared__ float s_min[AP_WAVES][4];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const unsigned stride = gridDim.x * 4u;
-  // two items of prefetch per wave (loads past the end re-read the last item)
-  auto load = [&](unsigned it) {
-    const unsigned c = it < items ? it : items - 1;
-    return reinterpret_cast<const float2 *>(item_src(kp, k_new, v_new, n_new, c))[lane];
+  const int hkv = kp.hkv;
+  const unsigned waves = gridDim.x * (unsigned)AP_WAVES;
+  const unsigned run = (items + waves - 1) / waves;
+  const unsigned begin = (blockIdx.x * (unsigned)AP_WAVES + w) * run;
+  if (begin >= items) return;
+  const unsigned end = begin + run < items ? begin + run : items;
+  auto next = [&](Item it) {
+    if (++it.i == n_new) {
+      it.i = 0;
+      if (++it.h == hkv) {
+        it.h = 0;
+        if (++it.b == batch) {
+          it.b = 0;
+          ++it.which;
+        }
+      }
+    }
+    return it;
   };
-  unsigned item = blockIdx.x * 4u + w;
-  float2 x0 = load(item), x1 = load(item + stride);
-  for (; item < items; item += stride) {
-    const float2 x = x0;
-    x0 = x1;
-    x1 = load(item + 2 * stride);
-    append_item(kp, vp, n_new, t0, item, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+  auto load = [&](const Item &it) {
+    return reinterpret_cast<const float2 *>(item_src(k_new, v_new, n_new, hkv, it))[lane];
+  };
+  Item it = item_of(begin, hkv, n_new, batch);
+  float2 x = load(it);
+  for (unsigned item = begin; item < end; ++item) {
+    const Item nx = item + 1 < end ? next(it) : it;
+    const float2 xn = load(nx);            // the last item re-reads its own row
+    if (it.which)
+      append_item(vp, n_new, t0, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+    else
+      append_item(kp, n_new, t0, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+    it = nx;
+    x = xn;
   }
 }
 
@@ -298,10 +374,10 @@ hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *
   const long long items = (long long)batch * n_new * kp.hkv * 2;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-  long long blocks = (items + 3) / 4;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kp, vp, k_new,
-                     v_new, n_new, t0, (unsigned)items);
+  long long blocks = (items + AP_WAVES - 1) / AP_WAVES;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(64 * AP_WAVES), 0, stream, kp, vp,
+                     k_new, v_new, n_new, t0, batch, (unsigned)items);
   return hipGetLastError();
 }
 
