@@ -136,6 +136,10 @@ typedef struct kvq_layer {
     int32_t tail_len;           /* N, multiple of 64, 0 = no tail */
     int32_t n_tokens;           /* T tokens already cached, 0 <= T <= capacity */
     int32_t tail_format;        /* kvq_tail_format of both tails */
+    const int32_t *seq_tokens;  /* NULL, or device [batch]: tokens of each
+                                   sequence (ragged batch), each in
+                                   [0, n_tokens]; n_tokens is then their
+                                   maximum.  See the entry points. */
 } kvq_layer;
 
 /* Byte sizes of the device buffers of K (which = 0) or V (which = 1):
@@ -144,11 +148,14 @@ typedef struct kvq_layer {
 kvq_status kvq_plane_bytes(const kvq_layer *layer, int32_t which, size_t *codes_bytes,
                            size_t *scales_bytes, size_t *mins_bytes, size_t *tail_bytes);
 
-/* Append n_new >= 1 tokens at positions n_tokens .. n_tokens+n_new-1.
+/* Append n_new >= 1 tokens at positions n_tokens .. n_tokens+n_new-1 (with
+ * seq_tokens: sequence b at seq_tokens[b] .. seq_tokens[b]+n_new-1).
  * k_new, v_new: device binary32 [B][n_new][Hkv][128].  Writes body codes,
- * scales, mins of every new token and, when tail_len > 0, its binary16 copy
+ * scales, mins of every new token and, when tail_len > 0, its 16-bit copy
  * into tail slot t mod tail_len (the newest token wins a slot).  The caller
- * advances n_tokens afterwards.  KVQ_ERR_CAPACITY if the rows do not fit. */
+ * advances n_tokens (and seq_tokens) afterwards.  KVQ_ERR_CAPACITY if
+ * n_tokens + n_new exceeds capacity; a sequence position past the capacity
+ * (a seq_tokens value above n_tokens breaks the contract) writes nothing. */
 kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const float *v_new,
                                int32_t n_new, void *stream);
 
@@ -160,7 +167,8 @@ kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const
  * (release notes, precision-tail section); the others are decoded rows (q*d,
  * fma(u, d, m), or the binary16 value) taken back to the raw basis: KVarN
  * x = (H y / 128) / w (release notes, KVarN section; H H = 128 I), low rank
- * x = P_h u (KV-COBRA explainer; coordinates past rank_h are zero).
+ * x = P_h u (KV-COBRA explainer; coordinates past rank_h are zero).  With
+ * seq_tokens, rows t >= seq_tokens[b] of sequence b are written as zeros.
  * Decode's output equals plain softmax attention over these K and V up to
  * rounding.  n_tokens == 0 writes nothing.  A read-back and measurement
  * path, not tuned for speed. */
@@ -171,7 +179,9 @@ kvq_status kvq_dequantize(const kvq_layer *layer, int32_t which, float *out, voi
  * codes/scales/mins are written, src is only read, the tails are untouched
  * (dst may share src's tail buffers).  src and dst must agree on batch,
  * n_kv_heads, capacity, tail_len, n_tokens, basis and w.  Every codec pair
- * is accepted; LOWRANK planes are not supported (KVQ_ERR_UNSUPPORTED). */
+ * is accepted; LOWRANK planes are not supported (KVQ_ERR_UNSUPPORTED).  A
+ * ragged batch is transcoded over n_tokens rows for every sequence (rows
+ * past a sequence's own count are re-encoded and stay unread). */
 kvq_status kvq_transcode_layer(const kvq_layer *src, const kvq_layer *dst, void *stream);
 
 /* Workspace needed by kvq_decode_attention for this layer's shapes and
@@ -191,7 +201,9 @@ size_t kvq_decode_workspace_bytes(const kvq_layer *layer, int32_t n_q_heads);
  * there); calls sharing a workspace must not overlap in time.  One kernel
  * launch: the split that finishes its (batch, kv head, head group) last
  * merges the splits into out.  Tokens t >= n_tokens - tail_len are read
- * from the tail. */
+ * from the tail.  With seq_tokens, sequence b attends over its own
+ * T_b = seq_tokens[b] tokens (tail: t >= T_b - tail_len); T_b == 0 gives a
+ * zero output. */
 kvq_status kvq_decode_attention(const kvq_layer *layer, const float *q, int32_t n_q_heads,
                                 float sm_scale, float *out, void *ws, size_t ws_bytes,
                                 void *stream);

@@ -73,6 +73,19 @@ class LayerCache:
             plane.tail = _ptr(b["tail"]).value
             self.bufs[name] = b
         self._ws = None
+        self.seq_tokens = None
+
+    def set_seq_tokens(self, seq):
+        """Ragged batch: seq is a device int32 tensor [B] of per-sequence token
+        counts (each <= n_tokens, which is their maximum), or None.  append()
+        advances it with n_tokens."""
+        if seq is None:
+            self.seq_tokens, self.desc.seq_tokens = None, None
+            return
+        if seq.dtype != torch.int32 or tuple(seq.shape) != (self.batch,) or seq.device != self.device:
+            raise ValueError("seq must be int32 [batch] on the layer's device")
+        self.seq_tokens = seq.contiguous()
+        self.desc.seq_tokens = self.seq_tokens.data_ptr()
 
     def _fill_spec(self, plane, spec):
         plane.basis = lib.BASIS_ID[spec.basis]
@@ -110,6 +123,12 @@ class LayerCache:
         n = k_new.shape[1]
         lib.quantize_append(self.desc, _ptr(k_new), _ptr(v_new), n, _stream(self.device, stream))
         self.desc.n_tokens += n
+        if self.seq_tokens is not None:
+            if stream is None:
+                self.seq_tokens.add_(n)
+            else:
+                with torch.cuda.stream(stream):
+                    self.seq_tokens.add_(n)
 
     def workspace(self, n_q_heads):
         need = lib.decode_workspace_bytes(self.desc, n_q_heads)

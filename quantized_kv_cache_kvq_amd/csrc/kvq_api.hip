@@ -268,6 +268,7 @@ kvq_status kvq_quantize_append(const kvq_layer *layer, const float *k_new, const
     return fail(KVQ_ERR_UNSUPPORTED, "append too large for one launch; split n_new");
   const PlaneArgs kp = plane_args(*layer, layer->k), vp = plane_args(*layer, layer->v);
   hipError_t e = launch_append(kp, vp, k_new, v_new, layer->batch, n_new, layer->n_tokens,
+                               layer->seq_tokens,
                                reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return ok();
@@ -283,8 +284,7 @@ kvq_status kvq_dequantize(const kvq_layer *layer, int32_t which, float *out, voi
       layer->n_kv_heads > 65535)
     return fail(KVQ_ERR_UNSUPPORTED, "batch or n_kv_heads above 65535");
   const PlaneArgs p = plane_args(*layer, which ? layer->v : layer->k);
-  const int n_tail = layer->tail_len < layer->n_tokens ? layer->tail_len : layer->n_tokens;
-  hipError_t e = launch_dequant(p, layer->batch, layer->n_tokens, n_tail, out,
+  hipError_t e = launch_dequant(p, layer->batch, layer->n_tokens, layer->seq_tokens, out,
                                 reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "dequantize launch");
   return ok();
@@ -425,6 +425,9 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
   a.part = reinterpret_cast<float *>(wsb + W.part);
   a.out = out;
   a.cnt = reinterpret_cast<unsigned *>(wsb + W.cnt);
+  a.seq = L.seq_tokens;
+  a.T = P.T;
+  a.N = L.tail_len;
   a.B = P.B;
   a.Hkv = P.Hkv;
   a.Hq = P.Hq;

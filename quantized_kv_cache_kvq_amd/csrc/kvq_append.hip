@@ -172,6 +172,7 @@ __device__ __forceinline__ void append_item(const PlaneArgs &p, int n_new, int t
   const int h = it.h, i = it.i, b = it.b;
   const int t = t0 + i;
   const int lane = threadIdx.x & 63;
+  if ((unsigned)t >= (unsigned)p.capacity) return;   // ragged position out of contract: no write
 
   // 1. precision tail: 16-bit raw copy (binary16 or bfloat16), slot t mod N,
   //    256-byte rows.  Only the newest N tokens of this call write: older
@@ -326,6 +327,7 @@ __global__ __launch_bounds__(64 * AP_WAVES) void append_kernel(PlaneArgs kp, Pla
                                                                const float *__restrict__ k_new,
                                                                const float *__restrict__ v_new,
                                                                int n_new, int t0, int batch,
+                                                               const int32_t *__restrict__ seq,
                                                                unsigned items) {
   __shared__ float xin[AP_WAVES][D];
   __shared__ float coords[AP_WAVES][D];
@@ -360,24 +362,27 @@ __global__ __launch_bounds__(64 * AP_WAVES) void append_kernel(PlaneArgs kp, Pla
   for (unsigned item = begin; item < end; ++item) {
     const Item nx = item + 1 < end ? next(it) : it;
     const float2 xn = load(nx);            // the last item re-reads its own row
+    // ragged batch: sequence b appends at its own position
+    const int tb = seq ? __builtin_amdgcn_readfirstlane(seq[it.b]) : t0;
     if (it.which)
-      append_item(vp, n_new, t0, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+      append_item(vp, n_new, tb, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
     else
-      append_item(kp, n_new, t0, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+      append_item(kp, n_new, tb, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
     it = nx;
     x = xn;
   }
 }
 
 hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
-                         const float *v_new, int batch, int n_new, int t0, hipStream_t stream) {
+                         const float *v_new, int batch, int n_new, int t0, const int32_t *seq,
+                         hipStream_t stream) {
   const long long items = (long long)batch * n_new * kp.hkv * 2;
   if (items <= 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   long long blocks = (items + AP_WAVES - 1) / AP_WAVES;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(64 * AP_WAVES), 0, stream, kp, vp,
-                     k_new, v_new, n_new, t0, batch, (unsigned)items);
+                     k_new, v_new, n_new, t0, batch, seq, (unsigned)items);
   return hipGetLastError();
 }
 

@@ -779,6 +779,15 @@ struct BodyLds<C, true> {
 // ------------------------------------------------------------- kernels ----
 
 
+// Tokens of sequence b in a ragged batch: body and tail counts of its own
+// T_b (the plan's ranges are for the longest sequence).
+__device__ __forceinline__ void seq_counts(const DecodeArgs &a, int b, int &body, int &tail) {
+  int Tb = a.seq[b];
+  Tb = Tb < 0 ? 0 : Tb > a.T ? a.T : Tb;
+  tail = a.N < Tb ? a.N : Tb;
+  body = Tb - tail;
+}
+
 // LR: per-head widths and codecs (low-rank planes, offsets from the head
 // tables); otherwise every plane has the configuration's fixed geometry.
 template <class C, bool LR>
@@ -806,6 +815,11 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, in
   const long long tps = (long long)a.tps_body * 64;
   io.t_begin = (long long)s * tps;
   io.t_end = io.t_begin + tps < a.body_tokens ? io.t_begin + tps : a.body_tokens;
+  if (a.seq) {
+    int body, tail;
+    seq_counts(a, b, body, tail);
+    if (io.t_end > body) io.t_end = body;
+  }
   io.part = a.part + (((long long)b * a.Hq + head0) * a.S_total + s) * PSTRIDE;
   io.part_head_stride = (long long)a.S_total * PSTRIDE;
   if constexpr (BodyLds<C>::INT_QK) attend_q<C>(io, lds);
@@ -827,6 +841,11 @@ __device__ __forceinline__ void run_tail(const DecodeArgs &a, int b, int kvh, in
   const long long tps = (long long)a.tps_tail * 64;
   io.t_begin = (long long)st * tps;
   io.t_end = io.t_begin + tps < a.tail_tokens ? io.t_begin + tps : a.tail_tokens;
+  if (a.seq) {
+    int body, tail;
+    seq_counts(a, b, body, tail);
+    if (io.t_end > tail) io.t_end = tail;
+  }
   io.part = a.part + (((long long)b * a.Hq + head0) * a.S_total + s) * PSTRIDE;
   io.part_head_stride = (long long)a.S_total * PSTRIDE;
   attend_range<C, BF>(io, lds);
@@ -936,7 +955,8 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
   const float M = fmaxf(mb, mt);
   const float wb = mb == NEG_INF ? 0.f : exp2f(mb - M);
   const float wt = mt == NEG_INF ? 0.f : exp2f(mt - M);
-  const float inv = 1.f / (wb * lb + wt * lt);
+  const float L = wb * lb + wt * lt;
+  const float inv = L > 0.f ? 1.f / L : 0.f;       // no tokens (empty sequence): zero output
   float2 o;
   o.x = (wb * ob0 + wt * ot0) * inv;
   o.y = (wb * ob1 + wt * ot1) * inv;
@@ -988,7 +1008,7 @@ __device__ __forceinline__ void fetch_args(const DecodeArgs &a) {
                "s"(a.q_tail), "s"(a.part));
   asm volatile("" ::"s"(a.k.codes), "s"(a.k.scales), "s"(a.k.mins), "s"(a.k.tail),
                "s"(a.k.capacity), "s"(a.k.tail_len), "s"(a.v.codes), "s"(a.v.scales),
-               "s"(a.v.mins), "s"(a.v.tail), "s"(a.k.tail_bf16));
+               "s"(a.v.mins), "s"(a.v.tail), "s"(a.k.tail_bf16), "s"(a.seq));
 }
 
 template <int HG, int KC, int VC>

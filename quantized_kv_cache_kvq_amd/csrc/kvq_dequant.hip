@@ -38,15 +38,24 @@ __device__ inline uint32_t field_of(const uint8_t *base, const HeadGeom &g, long
   return bits == 32 ? v : v & ((1u << bits) - 1u);
 }
 
-__global__ __launch_bounds__(64 * DQ_WAVES) void dequant_kernel(PlaneArgs p, int T, int n_tail,
+__global__ __launch_bounds__(64 * DQ_WAVES) void dequant_kernel(PlaneArgs p, int T,
+                                                                const int32_t *__restrict__ seq,
                                                                 float *__restrict__ out) {
   __shared__ float coords[DQ_WAVES][D];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * DQ_WAVES + wave;
   const int h = blockIdx.y, b = blockIdx.z;
   if (t >= T) return;
+  int Tb = T;                                      // this sequence's tokens
+  if (seq) {
+    const int s = seq[b];
+    Tb = s < 0 ? 0 : s > T ? T : s;
+  }
+  const int n_tail = p.tail_len < Tb ? p.tail_len : Tb;
   float x0 = 0.f, x1 = 0.f;
-  if (t >= T - n_tail) {
+  if (t >= Tb) {
+    // past this sequence's tokens: zeros
+  } else if (t >= Tb - n_tail) {
     // 16-bit ring row: 256-byte rows in the tiled layout (16-byte chunks)
     const long long plane = (long long)b * p.hkv + h;
     const uint8_t *ring = reinterpret_cast<const uint8_t *>(p.tail) + plane * p.tail_len * (2 * D);
@@ -118,10 +127,10 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void dequant_kernel(PlaneArgs p, int
 
 }  // namespace
 
-hipError_t launch_dequant(const PlaneArgs &p, int batch, int T, int n_tail, float *out,
+hipError_t launch_dequant(const PlaneArgs &p, int batch, int T, const int32_t *seq, float *out,
                           hipStream_t stream) {
   const dim3 grid((unsigned)((T + DQ_WAVES - 1) / DQ_WAVES), (unsigned)p.hkv, (unsigned)batch);
-  hipLaunchKernelGGL(dequant_kernel, grid, dim3(64 * DQ_WAVES), 0, stream, p, T, n_tail, out);
+  hipLaunchKernelGGL(dequant_kernel, grid, dim3(64 * DQ_WAVES), 0, stream, p, T, seq, out);
   return hipGetLastError();
 }
 

@@ -38,15 +38,19 @@ struct DecodeArgs {
   float *part;            // [B][Hq][S_total][PSTRIDE]
   float *out;             // [B][Hq][128] final output
   unsigned *cnt;          // [B][Hkv][NHG] finished-split counters (zero between calls)
+  const int32_t *seq;     // ragged batch: tokens of each sequence (null: all T)
+  int T, N;               // tokens (maximum over sequences), tail length
   PlaneArgs k, v;
 };
 
 hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
-                         const float *v_new, int batch, int n_new, int t0, hipStream_t stream);
+                         const float *v_new, int batch, int n_new, int t0, const int32_t *seq,
+                         hipStream_t stream);
 
 // Raw-basis binary32 view of plane p, out[B][T][hkv][128]; the newest
-// n_tail tokens come from the tail ring.
-hipError_t launch_dequant(const PlaneArgs &p, int batch, int T, int n_tail, float *out,
+// min(tail_len, T_b) tokens of sequence b come from the tail ring, rows
+// past T_b (ragged batch, seq non-null) are zero.
+hipError_t launch_dequant(const PlaneArgs &p, int batch, int T, const int32_t *seq, float *out,
                           hipStream_t stream);
 
 hipError_t launch_transcode(const PlaneArgs &src, const PlaneArgs &dst, int batch, int T,

@@ -49,6 +49,7 @@ class kvq_layer(ctypes.Structure):
         ("tail_len", ctypes.c_int32),
         ("n_tokens", ctypes.c_int32),
         ("tail_format", ctypes.c_int32),
+        ("seq_tokens", ctypes.c_void_p),
     ]
 
 
