@@ -779,6 +779,44 @@ struct BodyLds<C, true> {
 // ------------------------------------------------------------- kernels ----
 
 
+// Low-rank head tables of the decode's argument block (DecodeArgs is the
+// kernels' first argument), read from the argument segment at run-time
+// indices: indexing the by-value argument itself makes the compiler copy
+// the whole block to scratch.  K and V share the tables.
+template <class T>
+__device__ __forceinline__ T decode_arg_at(size_t byte_off, int i) {
+  typedef const __attribute__((address_space(4))) T *cptr;
+  typedef const __attribute__((address_space(4))) uint8_t *bptr;
+  return ((cptr)((bptr)__builtin_amdgcn_kernarg_segment_ptr() + byte_off))[i];
+}
+__device__ __forceinline__ int lr_rank(int h) {
+  return decode_arg_at<int16_t>(offsetof(DecodeArgs, k) + offsetof(PlaneArgs, hrank), h);
+}
+__device__ __forceinline__ int lr_codec(int h) {
+  return decode_arg_at<int8_t>(offsetof(DecodeArgs, k) + offsetof(PlaneArgs, hcodec), h);
+}
+// Geometry of low-rank plane (b, h): offsets are prefix sums over heads.
+__device__ __forceinline__ HeadGeom lr_geom(const DecodeArgs &a, int b, int h) {
+  long long rb_before = 0, nb_before = 0, rb_all = 0, nb_all = 0;
+  for (int i = 0; i < a.Hkv; ++i) {
+    const int r = lr_rank(i), c = lr_codec(i);
+    const int rb = row_bytes(c, r), nb = r / block_len(r);
+    if (i < h) { rb_before += rb; nb_before += nb; }
+    rb_all += rb;
+    nb_all += nb;
+  }
+  HeadGeom g;
+  g.codec = lr_codec(h);
+  g.n = lr_rank(h);
+  g.R = row_bytes(g.codec, g.n);
+  g.c = chunk_bytes(g.R);
+  g.L = block_len(g.n);
+  g.nblk = g.n / g.L;
+  g.codes_off = (long long)a.k.capacity * (b * rb_all + rb_before);
+  g.scales_off = (long long)a.k.capacity * (b * nb_all + nb_before);
+  return g;
+}
+
 // Tokens of sequence b in a ragged batch: body and tail counts of its own
 // T_b (the plan's ranges are for the longest sequence).
 __device__ __forceinline__ void seq_counts(const DecodeArgs &a, int b, int &body, int &tail) {
@@ -794,7 +832,7 @@ template <class C, bool LR>
 __device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
   long long kco, kso, vco, vso;
   if constexpr (LR) {
-    const HeadGeom gk = head_geom(a.k, b, kvh), gv = head_geom(a.v, b, kvh);
+    const HeadGeom gk = lr_geom(a, b, kvh), gv = gk;
     kco = gk.codes_off; kso = gk.scales_off;
     vco = gv.codes_off; vso = gv.scales_off;
   } else {
@@ -860,7 +898,7 @@ __device__ __forceinline__ void run_tail(const DecodeArgs &a, int b, int kvh, in
 // are in the stored basis and go back to the raw basis first (Hadamard
 // transform and 1/w for KVarN, P_h for low rank) before they meet the tail
 // partials.  `olow` holds 128 floats of LDS.
-__device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out, int b, int h,
+__device__ __forceinline__ void combine_head(const DecodeArgs &a, float *__restrict__ out, int b, int h,
                                     float *olow) {
   const int lane = threadIdx.x & 63;
   const long long bh = (long long)b * a.Hq + h;
@@ -938,7 +976,7 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
       ob0 = x0 * (1.f / 128.f) / wv[2 * lane];
       ob1 = x1 * (1.f / 128.f) / wv[2 * lane + 1];
     } else if (a.v.basis == KVQ_BASIS_LOWRANK) {
-      const int nv = a.v.hrank[g];
+      const int nv = lr_rank(g);
       olow[2 * lane] = 2 * lane < nv ? ob0 : 0.f;
       olow[2 * lane + 1] = 2 * lane + 1 < nv ? ob1 : 0.f;
       wave_sync_lds();
@@ -967,7 +1005,7 @@ __device__ inline void combine_head(const DecodeArgs &a, float *__restrict__ out
 // device-scope counter per unit in the workspace); the workgroup that
 // finishes its unit last merges the unit's heads (wave w takes head w of
 // the group) and re-arms the counter, so counters are zero between calls.
-__device__ inline void finish_split(const DecodeArgs &a, int b, int kvh, int hg, uint8_t *lds) {
+__device__ __forceinline__ void finish_split(const DecodeArgs &a, int b, int kvh, int hg, uint8_t *lds) {
   __shared__ unsigned s_last;
   __builtin_amdgcn_s_waitcnt(0);           // this thread's partial stores completed
   __syncthreads();
@@ -987,7 +1025,7 @@ __device__ inline void finish_split(const DecodeArgs &a, int b, int kvh, int hg,
 // the same launch (so the short tail work overlaps the body).  Grid:
 // x = split (tail splits first, then body splits), y = kv head * NHG +
 // head group, z = batch entry; one 32-bit division per workgroup.
-__device__ inline bool split_decode(const DecodeArgs &a, int &b, int &kvh, int &hg, int &s) {
+__device__ __forceinline__ bool split_decode(const DecodeArgs &a, int &b, int &kvh, int &hg, int &s) {
   const unsigned x = blockIdx.x, y = blockIdx.y;
   const bool tail = x < (unsigned)a.S_tail;
   s = tail ? a.S_body + (int)x : (int)x - a.S_tail;
@@ -1050,7 +1088,7 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(De
     if (a.k.tail_bf16) run_tail<HG, true>(a, b, kvh, hg, s, lds);
     else run_tail<HG, false>(a, b, kvh, hg, s, lds);
   } else {
-    const int codec = a.k.hcodec[kvh], rank = a.k.hrank[kvh];
+    const int codec = lr_codec(kvh), rank = lr_rank(kvh);
 #define KVQ_LR_DISPATCH(CC, RR)                                                           \
     if (codec == CC && rank == RR) run_body<Cfg<HG, CC, CC, RR, RR>, true>(a, b, kvh, hg, s, lds); else
     KVQ_LR_CASES(KVQ_LR_DISPATCH) {}

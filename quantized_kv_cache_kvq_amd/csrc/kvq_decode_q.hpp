@@ -194,11 +194,13 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     }
   }
 
-  // ---- tiles of this wave: t_begin + TT * (wave + NWAVE * i); 32-bit
-  // in-plane offsets; tokens past t_end load token t_end - 1 (masked later)
+  // ---- tiles of this wave: t_begin / TT + wave + NWAVE * i (tile indices;
+  // the loop carries the tile index, which keeps fewer values live than a
+  // token counter); 32-bit in-plane offsets; tokens past t_end load token
+  // t_end - 1 (masked later)
   const int t_end = (int)io.t_end;
-  const int first = (int)io.t_begin + TT * wave;
-  constexpr int stride = TT * NWAVE;
+  const int lim_tiles = (t_end + TT - 1) / TT;
+  int cur = (int)(io.t_begin / TT) + wave;
 
   uint64_t kr[NT][NKB];
   uint2 ksr[NT], kmr[NT], vsr[NT], vmr[NT];
@@ -259,8 +261,8 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   // compiler can count outstanding loads exactly and never has to drain
   // the prefetched tile early.
   {
-    const int lt0 = first < t_end ? first : (int)io.t_begin;
-    const int lim0 = first < t_end ? t_end - 1 - lt0 : 0;
+    const int lt0 = cur < lim_tiles ? cur * TT : (int)io.t_begin;
+    const int lim0 = cur < lim_tiles ? t_end - 1 - lt0 : 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) load_k_nt(lt0, lim0, nt);
     load_v(lt0, lim0);
@@ -335,9 +337,12 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     for (int dt = 0; dt < NDT; ++dt) O[rg][dt] = 0.f;
   }
 
-  for (int t0 = first; t0 < t_end; t0 += stride) {
-    const int tn = t0 + stride < t_end ? t0 + stride : t0;   // prefetch target
-    const int limn = t0 + stride < t_end ? t_end - 1 - tn : 0;
+  while (cur < lim_tiles) {
+    const int nxt = cur + NWAVE;
+    const bool more = nxt < lim_tiles;
+    const int t0 = cur * TT;
+    const int tn = more ? nxt * TT : t0;               // prefetch target
+    const int limn = more ? t_end - 1 - tn : 0;
     const int lim = t_end - 1 - t0;
 
     // ---- value row of token `lane` into LDS as offset-binary bytes; byte
@@ -514,6 +519,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
         O[rg][dt] = fmaf(O[rg][dt], alpha[rg], (ct[dt][2 * rg] + ct[dt][2 * rg + 1]) * bk);
     }
     wave_sync_lds();                    // LDS tiles are free for the next tile
+    cur = nxt;
   }
 
   // ---- close this wave: l and pm over the row's 16 lanes
