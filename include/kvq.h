@@ -184,6 +184,24 @@ kvq_status kvq_dequantize(const kvq_layer *layer, int32_t which, float *out, voi
  * past a sequence's own count are re-encoded and stay unread). */
 kvq_status kvq_transcode_layer(const kvq_layer *src, const kvq_layer *dst, void *stream);
 
+/* One decode step of a layer in one call: append one new token per
+ * sequence (k_new, v_new: device binary32 [B][1][Hkv][128], at position
+ * n_tokens, or seq_tokens[b]) and decode attention over the cache with it
+ * (n_tokens + 1 tokens, or seq_tokens[b] + 1).  Equal to
+ * kvq_quantize_append(layer, k_new, v_new, 1) followed by
+ * kvq_decode_attention on the layer with its counts advanced by one (the
+ * forum thread on decode bandwidth, second post: each step stores the new
+ * token's K and V and attends over all of them); the caller advances
+ * n_tokens (and seq_tokens) afterwards.  For plain and KVarN layers with one
+ * head group per kv head (n_q_heads / n_kv_heads in {1, 2, 4, 6, 8}) the
+ * append runs inside the decode launch: the one workgroup whose tiles hold
+ * the new token writes its rows before it reads; otherwise it is the two
+ * launches.  Workspace and errors as kvq_decode_attention;
+ * KVQ_ERR_CAPACITY when n_tokens + 1 exceeds capacity. */
+kvq_status kvq_append_decode(const kvq_layer *layer, const float *k_new, const float *v_new,
+                             const float *q, int32_t n_q_heads, float sm_scale, float *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace needed by kvq_decode_attention for this layer's shapes and
  * capacity (independent of n_tokens), in bytes.  Its first 64 KiB hold
  * split-completion counters: zero-fill a workspace once before its first

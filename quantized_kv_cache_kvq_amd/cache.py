@@ -161,6 +161,35 @@ class LayerCache:
         lib.dequantize(self.desc, {"k": 0, "v": 1}[which], _ptr(out), _stream(self.device, stream))
         return out
 
+    def append_decode(self, k_new, v_new, q, sm_scale, out=None, stream=None, ws=None):
+        """One decode step: append k_new, v_new (float32 [B, 1, Hkv, 128]) and
+        decode q (float32 [B, Hq, 128]) over the cache with the new token, in
+        one launch where the library can fuse them.  Advances n_tokens (and
+        seq_tokens)."""
+        k_new = k_new.contiguous()
+        v_new = v_new.contiguous()
+        if (k_new.dtype != torch.float32 or k_new.shape != v_new.shape
+                or tuple(k_new.shape) != (self.batch, 1, self.n_kv_heads, 128)):
+            raise ValueError("k_new/v_new must be float32 [B, 1, Hkv, 128]")
+        q = q.contiguous()
+        if q.dtype != torch.float32 or q.dim() != 3 or q.shape[0] != self.batch or q.shape[2] != 128:
+            raise ValueError("q must be float32 [B, Hq, 128]")
+        Hq = q.shape[1]
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace(Hq) if ws is None else ws
+        st = _stream(self.device, stream)
+        lib.append_decode(self.desc, _ptr(k_new), _ptr(v_new), _ptr(q), Hq, float(sm_scale), _ptr(out),
+                          _ptr(ws), ws.numel(), st)
+        self.desc.n_tokens += 1
+        if self.seq_tokens is not None:
+            if stream is None:
+                self.seq_tokens.add_(1)
+            else:
+                with torch.cuda.stream(stream):
+                    self.seq_tokens.add_(1)
+        return out
+
     def transcode(self, kcodec, vcodec, stream=None):
         """A new layer with K and V re-encoded; shares this layer's tails."""
         ks = PlaneSpec(kcodec, self.kspec.basis, self.kspec.w)

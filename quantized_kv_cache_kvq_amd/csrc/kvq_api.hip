@@ -322,12 +322,16 @@ size_t kvq_decode_workspace_bytes(const kvq_layer *layer, int32_t n_q_heads) {
   return ws_layout(*layer, n_q_heads, max_splits(*layer)).total;
 }
 
-kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, int32_t n_q_heads,
-                                       float sm_scale, float *out, void *ws, size_t ws_bytes,
-                                       int32_t body_splits, void *stream) {
-  kvq_status s = check_layer(layer);
-  if (s != KVQ_OK) return s;
-  const kvq_layer &L = *layer;
+}  // extern "C"
+
+namespace {
+
+// Decode of `layer` (already validated).  Fused step: k_new / v_new non-null
+// and layer.n_tokens already counting the new token (the kernel writes it);
+// seq_add is added to every seq_tokens entry.
+kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, float sm_scale,
+                       float *out, void *ws, size_t ws_bytes, int32_t body_splits, void *stream,
+                       const float *k_new, const float *v_new, int seq_add) {
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q / out is NULL");
   if (n_q_heads < 1 || n_q_heads % L.n_kv_heads)
     return fail(KVQ_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
@@ -426,6 +430,9 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
   a.out = out;
   a.cnt = reinterpret_cast<unsigned *>(wsb + W.cnt);
   a.seq = L.seq_tokens;
+  a.seq_add = seq_add;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.T = P.T;
   a.N = L.tail_len;
   a.B = P.B;
@@ -447,6 +454,43 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
                                reinterpret_cast<hipStream_t>(stream), P.prep, P.qsum);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, int32_t n_q_heads,
+                                       float sm_scale, float *out, void *ws, size_t ws_bytes,
+                                       int32_t body_splits, void *stream) {
+  kvq_status s = check_layer(layer);
+  if (s != KVQ_OK) return s;
+  return decode_impl(*layer, q, n_q_heads, sm_scale, out, ws, ws_bytes, body_splits, stream,
+                     nullptr, nullptr, 0);
+}
+
+kvq_status kvq_append_decode(const kvq_layer *layer, const float *k_new, const float *v_new,
+                             const float *q, int32_t n_q_heads, float sm_scale, float *out,
+                             void *ws, size_t ws_bytes, void *stream) {
+  kvq_status s = check_layer(layer);
+  if (s != KVQ_OK) return s;
+  if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  if ((long long)layer->n_tokens + 1 > layer->capacity)
+    return fail(KVQ_ERR_CAPACITY, "n_tokens %d + 1 exceeds capacity %d", layer->n_tokens,
+                layer->capacity);
+  kvq_layer after = *layer;
+  after.n_tokens = layer->n_tokens + 1;
+  const int G = n_q_heads > 0 && n_q_heads % layer->n_kv_heads == 0 ? n_q_heads / layer->n_kv_heads : 0;
+  const bool fused = G > 0 && decode_head_group(G) == G && layer->k.basis != KVQ_BASIS_LOWRANK;
+  if (fused)
+    return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, k_new, v_new, 1);
+  // not fusable here (several head groups per kv head read the same tiles,
+  // or low rank): the append launch, then the decode launch
+  const PlaneArgs kp = plane_args(*layer, layer->k), vp = plane_args(*layer, layer->v);
+  hipError_t e = launch_append(kp, vp, k_new, v_new, layer->batch, 1, layer->n_tokens,
+                               layer->seq_tokens, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, nullptr, nullptr, 1);
 }
 
 kvq_status kvq_decode_attention(const kvq_layer *layer, const float *q, int32_t n_q_heads,

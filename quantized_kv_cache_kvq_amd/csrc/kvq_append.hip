@@ -19,47 +19,8 @@
 
 namespace kvq {
 
-// All-reduce over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, dpp_f<0x128>(x));
-  x = fmaxf(x, dpp_f<0x124>(x));
-  x = fmaxf(x, dpp_f<0x122>(x));
-  return fmaxf(x, dpp_f<0x121>(x));
-}
-__device__ __forceinline__ float row_min16(float x) {
-  x = fminf(x, dpp_f<0x128>(x));
-  x = fminf(x, dpp_f<0x124>(x));
-  x = fminf(x, dpp_f<0x122>(x));
-  return fminf(x, dpp_f<0x121>(x));
-}
-
-// In-wave fast Walsh-Hadamard transform of 128 values, lane l holding
-// elements 2l (a) and 2l+1 (b).  Butterflies (u+v, u-v) at every stride give
-// the Sylvester (natural-order) H applied to the vector.
-__device__ inline void fwht128_wave(float &a, float &b) {
-  const int lane = threadIdx.x & 63;
-  float s = a + b, d = a - b;          // stride 1: inside the lane
-  a = s;
-  b = d;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {   // stride 2m: partner lane l ^ m
-    float pa = __shfl_xor(a, m, 64);
-    float pb = __shfl_xor(b, m, 64);
-    bool upper = (lane & m) != 0;
-    a = upper ? (pa - a) : (a + pa);
-    b = upper ? (pb - b) : (b + pb);
-  }
-}
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+#include "kvq_append_row.hpp"
+using namespace arow;
 
 // Items are plane-major, token-minor: item = ((K|V * B + b) * Hkv + h) * n_new
 // + i, so a workgroup's waves take consecutive new tokens of one plane and
@@ -86,81 +47,6 @@ __device__ __forceinline__ const float *item_src(const float *__restrict__ k_new
   return (it.which ? v_new : k_new) + (((long long)it.b * n_new + it.i) * hkv + it.h) * D;
 }
 
-// Per-block scale (and min), codes and bit-packed row of one token whose
-// stored coordinates are held two per lane (a = coordinate 2l, c = 2l + 1),
-// for a plain or KVarN plane of a fixed codec: blocks of 32 are the 16
-// lanes of a DPP row, so every reduction is a row reduction and nothing goes
-// through LDS except the 3/5/6-bit pack.  `rows` = rows before this
-// (b, kv head) plane.
-template <int BITS, int FAM>
-__device__ __forceinline__ void quantize_row(const PlaneArgs &p, long long rows, int t, float a, float c,
-                                             uint32_t *stage) {
-  constexpr int RB = row_bytes(FAM == FAM_0 ? KVQ_Q8_0 : KVQ_Q8_1, D) * BITS / 8;   // 16 * BITS
-  constexpr int CK = chunk_bytes(RB);
-  const int lane = threadIdx.x & 63;
-  const long long so = (rows + t) * 4 + (lane >> 4);
-  float d, m = 0.f;
-  if constexpr (FAM == FAM_0) {
-    const float amax = row_max16(fmaxf(fabsf(a), fabsf(c)));
-    constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
-    const uint16_t dh = f32_to_f16_bits(amax / qmax);
-    if ((lane & 15) == 0) p.scales[so] = dh;
-    d = f16_bits_to_f32(dh);
-  } else {
-    const float lo = row_min16(fminf(a, c)), hi = row_max16(fmaxf(a, c));
-    const uint16_t mh = f32_to_f16_bits(lo);
-    m = f16_bits_to_f32(mh);
-    constexpr float levels = (float)((1 << BITS) - 1);
-    const uint16_t dh = f32_to_f16_bits((hi - m) / levels);
-    if ((lane & 15) == 0) {
-      p.scales[so] = dh;
-      p.mins[so] = mh;
-    }
-    d = f16_bits_to_f32(dh);
-  }
-  constexpr uint32_t mask = (1u << BITS) - 1u;
-  uint32_t q0 = 0, q1 = 0;
-  if (d != 0.f) {
-    if constexpr (FAM == FAM_0) {
-      constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
-      q0 = (uint32_t)(int)fminf(fmaxf(rintf(a / d), -qmax), qmax);
-      q1 = (uint32_t)(int)fminf(fmaxf(rintf(c / d), -qmax), qmax);
-    } else {
-      constexpr float levels = (float)((1 << BITS) - 1);
-      q0 = (uint32_t)(int)fminf(fmaxf(rintf((a - m) / d), 0.f), levels);
-      q1 = (uint32_t)(int)fminf(fmaxf(rintf((c - m) / d), 0.f), levels);
-    }
-  }
-  // this lane's 2*BITS bits start at bit 2*BITS*lane of the row
-  const uint32_t v = (q0 & mask) | ((q1 & mask) << BITS);
-  uint8_t *tile = p.codes + rows * RB + (long long)(t / TILE) * TILE * RB;
-  const int tt = t % TILE;
-  if constexpr (BITS == 8 || BITS == 4 || BITS == 2 || BITS == 1) {
-    constexpr int K = 16 / BITS;                   // lanes per dword
-    uint32_t w = v << (2 * BITS * (lane % K));
-#pragma unroll
-    for (int o = 1; o < K; o <<= 1) w |= __shfl_xor(w, o, 64);
-    if (lane % K == 0) {
-      const int byte = 4 * (lane / K);
-      *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = w;
-    }
-  } else {
-    // 3, 5, 6 bits: OR each lane's field into the row's dwords in LDS
-    if (lane < RB / 4) stage[lane] = 0u;
-    wave_sync();
-    const int o = 2 * BITS * lane, k = o >> 5, sh = o & 31;
-    __hip_atomic_fetch_or(stage + k, v << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (sh + 2 * BITS > 32)
-      __hip_atomic_fetch_or(stage + k + 1, v >> (32 - sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    wave_sync();
-    if (lane < RB / 4) {
-      const int byte = 4 * lane;
-      *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = stage[lane];
-    }
-    wave_sync();                                   // stage is free for the next item
-  }
-}
-
 // One item, one wave; x = this lane's two raw channels (loaded by the
 // caller ahead of time); p is the item's plane (a kernel argument bound at
 // the call site, so its fields stay scalar loads of the argument buffer).
@@ -178,51 +64,23 @@ __device__ __forceinline__ void append_item(const PlaneArgs &p, int n_new, int t
   //    256-byte rows.  Only the newest N tokens of this call write: older
   //    ones in the same call would race for the slots they share with newer
   //    ones.
-  if (p.tail_len > 0 && i + p.tail_len >= n_new) {
-    const long long plane = (long long)b * hkv + h;
-    const int slot = t % p.tail_len;
-    const uint32_t pair =
-        p.tail_bf16 ? (uint32_t)f32_to_bf16_bits(x.x) | ((uint32_t)f32_to_bf16_bits(x.y) << 16)
-                    : (uint32_t)f32_to_f16_bits(x.x) | ((uint32_t)f32_to_f16_bits(x.y) << 16);
-    uint8_t *base = reinterpret_cast<uint8_t *>(p.tail) + plane * p.tail_len * (2 * D);
-    const int byte = 4 * lane;
-    *reinterpret_cast<uint32_t *>(base + tiled_offset(slot, byte / 16, 2 * D, 16) + byte % 16) = pair;
-  }
+  if (p.tail_len > 0 && i + p.tail_len >= n_new) store_tail(p, (long long)b * hkv + h, t, x);
 
   // 2. plain and KVarN planes: coordinates stay in registers (the rotation
   //    is an in-wave transform), codec fixed at compile time per case
   if (p.basis != KVQ_BASIS_LOWRANK) {
-    float a = x.x, c = x.y;
-    if (p.basis == KVQ_BASIS_HADAMARD) {
-      const float *w = p.w + (long long)h * D;
-      a *= w[2 * lane];
-      c *= w[2 * lane + 1];
-      fwht128_wave(a, c);
-    }
+    float a, c;
+    stored_coords(p, h, x, a, c);
     const long long rows = ((long long)b * hkv + h) * p.capacity;
     uint32_t *stage = reinterpret_cast<uint32_t *>(coords);
     switch (p.codec) {
-      case KVQ_F16: {
-        // binary16 row: dword `lane` holds coordinates 2*lane, 2*lane+1
-        const uint32_t pair = (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(c) << 16);
-        const int byte = 4 * lane;
-        *reinterpret_cast<uint32_t *>(p.codes + rows * (2 * D) + tiled_offset(t, byte / 16, 2 * D, 16) +
-                                      byte % 16) = pair;
-        break;
-      }
-      case KVQ_Q8_0: quantize_row<8, FAM_0>(p, rows, t, a, c, stage); break;
-      case KVQ_Q6_0: quantize_row<6, FAM_0>(p, rows, t, a, c, stage); break;
-      case KVQ_Q5_0: quantize_row<5, FAM_0>(p, rows, t, a, c, stage); break;
-      case KVQ_Q4_0: quantize_row<4, FAM_0>(p, rows, t, a, c, stage); break;
-      case KVQ_Q3_0: quantize_row<3, FAM_0>(p, rows, t, a, c, stage); break;
-      case KVQ_Q2_0: quantize_row<2, FAM_0>(p, rows, t, a, c, stage); break;
-      case KVQ_Q8_1: quantize_row<8, FAM_1>(p, rows, t, a, c, stage); break;
-      case KVQ_Q6_1: quantize_row<6, FAM_1>(p, rows, t, a, c, stage); break;
-      case KVQ_Q5_1: quantize_row<5, FAM_1>(p, rows, t, a, c, stage); break;
-      case KVQ_Q4_1: quantize_row<4, FAM_1>(p, rows, t, a, c, stage); break;
-      case KVQ_Q3_1: quantize_row<3, FAM_1>(p, rows, t, a, c, stage); break;
-      case KVQ_Q2_1: quantize_row<2, FAM_1>(p, rows, t, a, c, stage); break;
-      case KVQ_Q1_1: quantize_row<1, FAM_1>(p, rows, t, a, c, stage); break;
+#define KVQ_ROW_CASE(CC) case CC: store_row<CC>(p, rows, t, a, c, stage); break;
+      KVQ_ROW_CASE(KVQ_F16)
+      KVQ_ROW_CASE(KVQ_Q8_0) KVQ_ROW_CASE(KVQ_Q6_0) KVQ_ROW_CASE(KVQ_Q5_0) KVQ_ROW_CASE(KVQ_Q4_0)
+      KVQ_ROW_CASE(KVQ_Q3_0) KVQ_ROW_CASE(KVQ_Q2_0)
+      KVQ_ROW_CASE(KVQ_Q8_1) KVQ_ROW_CASE(KVQ_Q6_1) KVQ_ROW_CASE(KVQ_Q5_1) KVQ_ROW_CASE(KVQ_Q4_1)
+      KVQ_ROW_CASE(KVQ_Q3_1) KVQ_ROW_CASE(KVQ_Q2_1) KVQ_ROW_CASE(KVQ_Q1_1)
+#undef KVQ_ROW_CASE
       default: break;
     }
     return;

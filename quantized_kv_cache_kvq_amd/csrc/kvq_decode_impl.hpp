@@ -22,6 +22,10 @@
 #include "kvq_internal.hpp"
 
 namespace kvq {
+#include "kvq_append_row.hpp"
+}
+
+namespace kvq {
 
 constexpr int NWAVE = DECODE_WG_WAVES;
 constexpr int WG = 64 * NWAVE;
@@ -820,7 +824,7 @@ __device__ __forceinline__ HeadGeom lr_geom(const DecodeArgs &a, int b, int h) {
 // Tokens of sequence b in a ragged batch: body and tail counts of its own
 // T_b (the plan's ranges are for the longest sequence).
 __device__ __forceinline__ void seq_counts(const DecodeArgs &a, int b, int &body, int &tail) {
-  int Tb = a.seq[b];
+  int Tb = a.seq[b] + a.seq_add;
   Tb = Tb < 0 ? 0 : Tb > a.T ? a.T : Tb;
   tail = a.N < Tb ? a.N : Tb;
   body = Tb - tail;
@@ -1049,6 +1053,44 @@ __device__ __forceinline__ void fetch_args(const DecodeArgs &a) {
                "s"(a.v.mins), "s"(a.v.tail), "s"(a.k.tail_bf16), "s"(a.seq));
 }
 
+// Fused step (a.k_new non-null): the new token of sequence b sits at
+// position t (its count before the step); the one workgroup whose tiles hold
+// it (the tail split of ring slot t mod N, or without a tail the body split
+// of row t) writes its K row (wave 0) and V row (wave 1) exactly as the
+// append kernel does, then waits for the stores before any wave loads.  Only
+// launched with one head group per kv head, so no other workgroup reads
+// those tiles.
+template <int CODEC>
+__device__ __forceinline__ void fused_row(const PlaneArgs &p, const float *x_new, int b, int kvh, int t,
+                                          uint8_t *lds) {
+  const int lane = threadIdx.x & 63;
+  const long long plane = (long long)b * p.hkv + kvh;
+  const float2 x = reinterpret_cast<const float2 *>(x_new + plane * D)[lane];
+  if (p.tail_len > 0) arow::store_tail(p, plane, t, x);
+  float ac, cc;
+  arow::stored_coords(p, kvh, x, ac, cc);
+  arow::store_row<CODEC>(p, plane * p.capacity, t, ac, cc,
+                         reinterpret_cast<uint32_t *>(lds) + (threadIdx.x >> 6) * 32);
+}
+
+template <int KC, int VC>
+__device__ __forceinline__ void fused_append(const DecodeArgs &a, int b, int kvh, int s, bool tail,
+                                             uint8_t *lds) {
+  int t = a.T - 1;
+  if (a.seq) {
+    const int sb = a.seq[b];
+    t = sb < 0 ? 0 : sb > a.T - 1 ? a.T - 1 : sb;
+  }
+  const bool mine = a.N > 0 ? tail && (s - a.S_body) == (t % a.N) / (a.tps_tail * 64)
+                            : !tail && s == t / (a.tps_body * 64);
+  if (!mine) return;
+  const int w = threadIdx.x >> 6;
+  if (w == 0) fused_row<KC>(a.k, a.k_new, b, kvh, t, lds);
+  else if (w == 1) fused_row<VC>(a.v, a.v_new, b, kvh, t, lds);
+  __builtin_amdgcn_s_waitcnt(0);           // the rows are in L2 before any wave loads
+  __syncthreads();
+}
+
 template <int HG, int KC, int VC>
 __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs a) {
   using CB = Cfg<HG, KC, VC, D, D>;
@@ -1056,7 +1098,9 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax<BodyLds<CB>::bytes, CT::LDS_BYTES>::value];
   int b, kvh, hg, s;
   fetch_args(a);
-  if (split_decode(a, b, kvh, hg, s)) {
+  const bool tail = split_decode(a, b, kvh, hg, s);
+  if (a.k_new) fused_append<KC, VC>(a, b, kvh, s, tail, lds);
+  if (tail) {
     if (a.k.tail_bf16) run_tail<HG, true>(a, b, kvh, hg, s, lds);
     else run_tail<HG, false>(a, b, kvh, hg, s, lds);
   }

@@ -39,7 +39,10 @@ struct DecodeArgs {
   float *out;             // [B][Hq][128] final output
   unsigned *cnt;          // [B][Hkv][NHG] finished-split counters (zero between calls)
   const int32_t *seq;     // ragged batch: tokens of each sequence (null: all T)
+  int seq_add;            // added to every seq entry (1 when a token was just appended)
   int T, N;               // tokens (maximum over sequences), tail length
+  const float *k_new;     // fused step (non-null): the new token's K and V rows
+  const float *v_new;     // [B][Hkv][128], written before the decode reads
   PlaneArgs k, v;
 };
 

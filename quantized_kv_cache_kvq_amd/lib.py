@@ -78,6 +78,10 @@ _SIGS = {
     "kvq_dequantize": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p]),
     "kvq_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kvq_layer), ctypes.c_int32]),
+    "kvq_append_decode": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]),
     "kvq_decode_attention": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
@@ -156,6 +160,11 @@ def dequantize(layer, which, out_ptr, stream):
 
 def decode_workspace_bytes(layer, n_q_heads):
     return load().kvq_decode_workspace_bytes(ctypes.byref(layer), n_q_heads)
+
+
+def append_decode(layer, k_ptr, v_ptr, q_ptr, n_q_heads, sm_scale, out_ptr, ws_ptr, ws_bytes, stream):
+    check(load().kvq_append_decode(ctypes.byref(layer), k_ptr, v_ptr, q_ptr, n_q_heads,
+                                   ctypes.c_float(sm_scale), out_ptr, ws_ptr, ws_bytes, stream))
 
 
 def decode_attention(layer, q_ptr, n_q_heads, sm_scale, out_ptr, ws_ptr, ws_bytes, stream,

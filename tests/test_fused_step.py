@@ -1,0 +1,135 @@
+"""GPU parity of the one-call decode step (kvq_append_decode): append one
+token per sequence and decode over the cache with it.
+
+For each case a layer holding T0 tokens (the oracle's encoding, uploaded)
+takes one step; then
+ - its stored bytes (codes, scales, mins, tail ring) equal the oracle's
+   encoding of the T0 + 1 tokens bit for bit;
+ - its output equals, bit for bit, that of a twin layer that ran the append
+   and the decode as two calls, and the oracle's decode over T0 + 1 tokens
+   within the decode tolerance.
+Cases: the new token landing in the tail ring (T0 below, at and past the
+tail length, slot wrap), no tail (the new row read by the last body split),
+plain and KVarN bodies, 3/5/6-bit rows (LDS packing inside the launch),
+binary16 and bfloat16 tails, a ragged batch, and the two-launch path (two
+head groups per kv head; low rank)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.layer as OL
+import synth
+from quantized_kv_cache_kvq_amd.cache import LayerCache
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(wl, cap, gk, gv, gpu, N, fmt):
+    return LayerCache(wl.B, wl.Hkv, cap, N, gk, gv, gpu, tail_format=fmt)
+
+
+def _upload(cache, name, x, spec, Ts, N, cap, fmt):
+    B, _, Hkv, _ = x.shape
+    enc = [[OL.encode_head(x[b, :Ts[b], h, :], spec, h) for h in range(Hkv)] for b in range(B)]
+    tail = None
+    if N > 0:
+        ring = np.concatenate([OL.tail_ring(x[b:b + 1, :Ts[b]], N, fmt=fmt) for b in range(B)])
+        tail = OL.pack_tail(ring, fmt=fmt)
+    H.upload(cache, name, OL.pack_plane(enc, spec, cap), tail)
+
+
+CASES = [
+    # name, kcodec, vcodec, Hq, T0, N, tail format, ragged
+    ("gqa4_q8k_q4v_tail1024", None, None, 8, 300, 128, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", None, None, 8, 127, 128, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", None, None, 8, 128, 128, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", None, None, 8, 0, 64, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", "q4_0", "q4_0", 8, 700, 0, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", "q6_0", "q6_0", 8, 257, 0, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", "q5_1", "q5_1", 8, 64, 64, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", "q8_0", "q3_0", 12, 333, 64, "bf16", False),
+    ("kvarn_q3_tail2048", None, None, 12, 500, 128, "f16", False),
+    ("vbr_32layer", "f16", "f16", 8, 190, 64, "f16", False),
+    ("gqa4_q8k_q4v_tail1024", None, None, 8, 0, 128, "f16", True),
+    ("gqa4_q8k_q4v_tail1024", "q4_0", "q4_0", 8, 0, 0, "f16", True),
+    ("gqa4_q8k_q4v_tail1024", None, None, 32, 200, 64, "f16", False),   # two head groups
+]
+
+
+@pytest.mark.parametrize("name,kc,vc,Hq,T0,N,fmt,ragged", CASES)
+def test_step_matches_two_calls_and_oracle(gpu, name, kc, vc, Hq, T0, N, fmt, ragged):
+    B = 3 if ragged else 2
+    Ts = [T0 + 90, T0 + 7, T0] if ragged else [T0] * B
+    wl = synth.WORKLOADS[name].with_(B=B, Hkv=2, Hq=Hq, T=max(Ts) + 1, N=N)
+    k = synth.layer_rows(wl, 0, "k").numpy()
+    v = synth.layer_rows(wl, 0, "v").numpy()
+    q = synth.queries(wl, 0)
+    gk, gv, ok_, ov = H.specs(wl, kcodec=kc, vcodec=vc)
+    cap = (max(Ts) + 1 + 63) // 64 * 64
+    kn = torch.from_numpy(np.stack([k[b, Ts[b]:Ts[b] + 1] for b in range(B)])).to(gpu)
+    vn = torch.from_numpy(np.stack([v[b, Ts[b]:Ts[b] + 1] for b in range(B)])).to(gpu)
+    outs, caches = [], []
+    for fused in (True, False):
+        c = _layer(wl, cap, gk, gv, gpu, N, fmt)
+        _upload(c, "k", k, ok_, Ts, N, cap, fmt)
+        _upload(c, "v", v, ov, Ts, N, cap, fmt)
+        c.n_tokens = max(Ts)
+        if ragged:
+            c.set_seq_tokens(torch.tensor(Ts, dtype=torch.int32, device=gpu))
+        if fused:
+            out = c.append_decode(kn, vn, q.to(gpu), wl.sm_scale)
+        else:
+            c.append(kn, vn)
+            out = c.decode(q.to(gpu), wl.sm_scale)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        caches.append(c)
+    assert np.array_equal(outs[0], outs[1]), "one-call step differs from append + decode"
+    T1 = [t + 1 for t in Ts]
+    for name_, x, spec in (("k", k, ok_), ("v", v, ov)):
+        dev = H.download(caches[0], name_)
+        if spec.basis == "hadamard":
+            # rotated rows: the tie rule on the new row (equal counts here)
+            encs, _ = H.unpack(caches[0], name_, spec, T1[0])
+            for b in range(B):
+                for h in range(2):
+                    H.check_rotated_head(x[b, :T1[b], h, :], encs[b][h], spec, h)
+        else:
+            enc = [[OL.encode_head(x[b, :T1[b], h, :], spec, h) for h in range(2)] for b in range(B)]
+            packed = OL.pack_plane(enc, spec, cap)
+            assert np.array_equal(dev["codes"][: packed["codes"].size], packed["codes"]), name_
+            for key in ("scales", "mins"):
+                if packed.get(key) is not None:
+                    assert np.array_equal(dev[key], packed[key]), (name_, key)
+        if N > 0:
+            ring = np.concatenate([OL.tail_ring(x[b:b + 1, :T1[b]], N, fmt=fmt) for b in range(B)])
+            assert np.array_equal(dev["tail"], OL.pack_tail(ring, fmt=fmt)), name_
+    ref = np.zeros(outs[0].shape)
+    for b in range(B):
+        kb, vb = k[b:b + 1, :T1[b]], v[b:b + 1, :T1[b]]
+        ref[b] = OL.decode(q.numpy()[b:b + 1], OL.encode_plane(kb, ok_), OL.encode_plane(vb, ov),
+                           OL.tail_ring(kb, N, fmt=fmt) if N else None,
+                           OL.tail_ring(vb, N, fmt=fmt) if N else None, ok_, ov, T1[b], N, wl.sm_scale)[0]
+    err = float(np.max(np.abs(outs[0].astype(np.float64) - ref)))
+    assert err <= H.ATOL, err
+
+
+def test_lowrank_step_two_launches(gpu):
+    wl = synth.WORKLOADS["lowrank_1bpd"].with_(B=2, T=301, N=0)
+    k = synth.layer_rows(wl, 0, "k").numpy()
+    v = synth.layer_rows(wl, 0, "v").numpy()
+    q = synth.queries(wl, 0)
+    gk, gv, ok_, ov = H.specs(wl)
+    cache = H.new_cache(wl, 320, gk, gv, gpu, N=0)
+    _upload(cache, "k", k, ok_, [300, 300], 0, 320, "f16")
+    _upload(cache, "v", v, ov, [300, 300], 0, 320, "f16")
+    cache.n_tokens = 300
+    out = cache.append_decode(torch.from_numpy(k[:, 300:301].copy()).to(gpu),
+                              torch.from_numpy(v[:, 300:301].copy()).to(gpu), q.to(gpu), wl.sm_scale)
+    torch.cuda.synchronize()
+    ref = OL.decode(q.numpy(), OL.encode_plane(k, ok_), OL.encode_plane(v, ov), None, None, ok_, ov,
+                    301, 0, wl.sm_scale)
+    assert cache.n_tokens == 301
+    assert float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))) <= H.ATOL
