@@ -2,9 +2,10 @@
 """Decode-step benchmark of the packed KV cache on one MI355X.
 
 A step is one pass of the hot path over one synthetic batch: append the new
-token's K and V to every layer (quantise, pack, tail copy), decode attention
-of every query head over the whole cache, and, for the mixed-codec workload,
-one layer transcode.  Inputs are resident in HBM before timing starts.  To
+token's K and V to every layer (quantise, pack, tail copy) and decode
+attention of every query head over the whole cache -- one kvq_append_decode
+call per layer, a single launch where the library fuses the two -- and, for
+the mixed-codec workload, one layer transcode.  Inputs are resident in HBM before timing starts.  To
 keep the step honest about HBM (the 256 MB Infinity Cache would otherwise
 hold a 57 MB cache), consecutive steps rotate over replicas of the cache
 whose total size exceeds the Infinity Cache.
@@ -337,6 +338,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=synth.ORDER)
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP graph replays of the step instead of eager launches")
     ap.add_argument("--prefill", action="store_true",
                     help="measure prefill-scale append and layer transcode instead")
     ap.add_argument("--quality", action="store_true",
@@ -387,8 +390,7 @@ def main():
         layers = reps[i % len(reps)]
         for li, c in enumerate(layers):
             c.n_tokens = wl.T - 1
-            c.append(news[li][0], news[li][1])
-            c.decode(qs[li], wl.sm_scale, out=outs[li])
+            c.append_decode(news[li][0], news[li][1], qs[li], wl.sm_scale, out=outs[li])
         if transcode_dst is not None:
             src, dst = transcode_dst
             layers[src].transcode_into(dst)
@@ -397,24 +399,46 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    def timed(instrument):
+    # --graph: the step replayed as a HIP graph (one graph per cache
+    # replica, captured after the warm-up), as a serving loop that captures
+    # its step would run it.  The step's kernels allocate nothing and record
+    # no memset, so a replay does exactly what the eager step does.  On this
+    # one-launch step a replay costs more than the eager launch, so eager is
+    # the default.
+    graphs = None
+    if args.graph:
+        graphs = []
+        for r in range(len(reps)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        for i in range(max(args.warmup, len(reps))):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+    def timed(instrument, use_graphs):
         if instrument:
             lib.timing_begin(args.steps * len(codecs))
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         t_start.record(stream)
         for i in range(args.steps):
-            step(i)
+            if use_graphs:
+                graphs[i % len(graphs)].replay()
+            else:
+                step(i)
         t_end.record(stream)
         torch.cuda.synchronize()
         ms = t_start.elapsed_time(t_end) / args.steps
         return (ms,) + (lib.timing_end() if instrument else (0.0, 0))
 
-    # timed region: K whole steps.  Then the same K steps again with every
-    # split-K attention launch stamped by HIP events (hipExtLaunchKernel, on
-    # the stream it runs on) for the kernel's own average duration.
-    ms_per_step, _, _ = timed(False)
-    ms_instr, kern_ms, kern_n = timed(True)
+    # timed region: K whole steps (graph replays with --graph).  Then K
+    # eager steps with every split-K attention launch stamped by HIP events
+    # (hipExtLaunchKernel, on the stream it runs on) for the kernel's own
+    # average duration.
+    ms_per_step, _, _ = timed(False, graphs is not None)
+    ms_instr, kern_ms, kern_n = timed(True, False)
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     ctx_tok_s = wl.B * wl.T * len(codecs) / (ms_per_step * 1e-3)
@@ -430,7 +454,7 @@ def main():
                 "traffic": measured_traffic(wl.name),
                 "kernel": "split-K decode attention (kvq::decode_kernel / decode_lowrank_kernel)",
                 "avg_launch_us": round(avg_ms * 1e3, 2), "launches": kern_n,
-                "ms_per_step_instrumented": round(ms_instr, 5),
+                "ms_per_step_eager_instrumented": round(ms_instr, 5),
                 "algorithmic_bytes_per_launch": per_launch}
     cpu = None
     if not args.no_cpu_baseline:
@@ -442,7 +466,8 @@ def main():
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic (seeded), resident in HBM; %d cache replicas rotated per step" % replicas,
+        "data": "synthetic (seeded), resident in HBM; %d cache replicas rotated per step; %s"
+                % (replicas, "eager launches" if graphs is None else "step replayed as a HIP graph"),
         "config": {"workload": wl.name, "batch": wl.B, "kv_heads": wl.Hkv, "q_heads": wl.Hq,
                    "context": wl.T, "tail": wl.N, "k_codec": wl.kcodec or "per-head",
                    "v_codec": wl.vcodec or "per-head", "basis": wl.basis, "layers": len(codecs),

@@ -169,6 +169,31 @@ constexpr int MAX_BODY_SPLITS = 1024;
 constexpr int MAX_TAIL_SPLITS = 64;
 constexpr int TAIL_TT = 64;
 constexpr int TAIL_TILES_PER_SPLIT = DECODE_WG_WAVES;
+// Fixed cost of one wave tile in the split planner, in bytes of streaming
+// (about one loaded memory round trip per tile at the per-wave rate seen on
+// MI355X).
+constexpr double PLAN_TILE_COST = 16384.0;
+
+// Body bytes per token of a layer (codes, scales, mins of K and V; the mean
+// over kv heads for low rank).
+double body_token_bytes(const kvq_layer &L) {
+  double sum = 0.0;
+  for (const kvq_plane *p : {&L.k, &L.v}) {
+    if (p->basis == KVQ_BASIS_LOWRANK) {
+      double t = 0.0;
+      for (int h = 0; h < L.n_kv_heads; ++h) {
+        const int r = p->rank[h], c = p->head_codec[h], nb = r / block_len(r);
+        t += row_bytes(c, r) + nb * 2 * (codec_family(c) == FAM_1 ? 2 : 1);
+      }
+      sum += t / L.n_kv_heads;
+    } else {
+      const int c = p->codec;
+      sum += row_bytes(c, KVQ_HEAD_DIM) +
+             (c == KVQ_F16 ? 0 : (KVQ_HEAD_DIM / 32) * 2 * (codec_family(c) == FAM_1 ? 2 : 1));
+    }
+  }
+  return sum;
+}
 
 int max_splits(const kvq_layer &L) {
   const int tt = decode_tile_tokens(L.k.codec, L.v.codec, L.k.basis);
@@ -371,21 +396,34 @@ kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, fl
     body_want = body_splits;
   } else if (body_tiles > 0) {
     // One round of workgroups (the resident workgroups of all CUs hold the
-    // whole grid) with the same number of body tiles for every wave: tiles
-    // per split is a multiple of the waves per workgroup, the smallest that
-    // leaves a slot per unit for the tail; the tail takes the slots left.
+    // whole grid), split between body and tail so that the slowest wave is
+    // as fast as possible.  Wave w of a split takes tiles w, w + 8, ...; a
+    // wave's time is modelled as its tile count times (a fixed per-tile
+    // cost, mostly one memory round trip, + the tile's bytes).  A binary16
+    // tail tile holds 2.5x the bytes of a q8/q4 body tile, so one tail
+    // split per unit would make the tail wave the slowest.  Ties keep the
+    // fewest tail splits.
     const int per_unit = (DECODE_WG_PER_CU * device_cus()) / units;
-    const int need_tail = tail_tiles > 0 ? 1 : 0;
-    for (int tps = DECODE_WG_WAVES;; tps += DECODE_WG_WAVES) {
-      const int sb = (body_tiles + tps - 1) / tps;
-      if (sb + need_tail <= per_unit || sb == 1) {
-        body_want = sb;
-        if (tail_tiles > 0) {
-          int room = per_unit - sb;
-          if (room < 1) room = 1;
-          if (tail_want > room) tail_want = room;
-        }
-        break;
+    const double cb = PLAN_TILE_COST + (double)P.tt_body * body_token_bytes(L);
+    const double ct = PLAN_TILE_COST + (double)TAIL_TT * 2 * 2 * KVQ_HEAD_DIM;
+    int st_hi = tail_tiles < MAX_TAIL_SPLITS ? tail_tiles : MAX_TAIL_SPLITS;
+    if (st_hi > per_unit - 1) st_hi = per_unit - 1;
+    const int st_lo = tail_tiles > 0 ? 1 : 0;
+    if (st_hi < st_lo) st_hi = st_lo;
+    double best = -1.0;
+    for (int st = st_lo; st <= st_hi; ++st) {
+      int sb = per_unit - st;
+      if (sb < 1) sb = 1;
+      if (sb > body_tiles) sb = body_tiles;
+      const int tpb = (body_tiles + sb - 1) / sb;
+      const int tpt = st > 0 ? (tail_tiles + st - 1) / st : 0;
+      const double wb = (double)((tpb + DECODE_WG_WAVES - 1) / DECODE_WG_WAVES) * cb;
+      const double wt = (double)((tpt + DECODE_WG_WAVES - 1) / DECODE_WG_WAVES) * ct;
+      const double cost = wb > wt ? wb : wt;
+      if (best < 0.0 || cost < best) {
+        best = cost;
+        body_want = (body_tiles + tpb - 1) / tpb;
+        tail_want = st;
       }
     }
   }
