@@ -116,10 +116,17 @@ PlaneArgs plane_args(const kvq_layer &L, const kvq_plane &p) {
   a.tail_len = L.tail_len;
   a.tail_bf16 = L.tail_format == KVQ_TAIL_BF16;
   if (p.basis == KVQ_BASIS_LOWRANK) {
+    int rows = 0, blks = 0;
     for (int h = 0; h < L.n_kv_heads; ++h) {
       a.hcodec[h] = (int8_t)p.head_codec[h];
       a.hrank[h] = (int16_t)p.rank[h];
+      a.hrow_before[h] = rows;
+      a.hblk_before[h] = blks;
+      rows += row_bytes(p.head_codec[h], p.rank[h]);
+      blks += p.rank[h] / block_len(p.rank[h]);
     }
+    a.row_all = rows;
+    a.blk_all = blks;
     a.codec = -1;
   }
   return a;

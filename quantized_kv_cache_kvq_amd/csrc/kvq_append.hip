@@ -51,9 +51,9 @@ __device__ __forceinline__ const float *item_src(const float *__restrict__ k_new
 // caller ahead of time); p is the item's plane (a kernel argument bound at
 // the call site, so its fields stay scalar loads of the argument buffer).
 // The LDS arrays are this wave's own.
+template <bool LR>
 __device__ __forceinline__ void append_item(const PlaneArgs &p, int n_new, int t0, const Item &it,
-                                            float2 x, float *xin, float *coords, uint8_t *codes,
-                                            float *s_scale, float *s_min) {
+                                            float2 x, float *xin, float *coords, uint8_t *codes) {
   const int hkv = p.hkv;
   const int h = it.h, i = it.i, b = it.b;
   const int t = t0 + i;
@@ -68,7 +68,7 @@ __device__ __forceinline__ void append_item(const PlaneArgs &p, int n_new, int t
 
   // 2. plain and KVarN planes: coordinates stay in registers (the rotation
   //    is an in-wave transform), codec fixed at compile time per case
-  if (p.basis != KVQ_BASIS_LOWRANK) {
+  if (!LR || p.basis != KVQ_BASIS_LOWRANK) {
     float a, c;
     stored_coords(p, h, x, a, c);
     const long long rows = ((long long)b * hkv + h) * p.capacity;
@@ -85,93 +85,124 @@ __device__ __forceinline__ void append_item(const PlaneArgs &p, int n_new, int t
     }
     return;
   }
+  if constexpr (LR) {
 
   // 3. low rank: u = P_h^T x through LDS, then per-head width and codec
-  const HeadGeom g = head_geom(p, b, h);
   xin[2 * lane] = x.x;
   xin[2 * lane + 1] = x.y;
   wave_sync();
   {
-    const uint16_t *P = p.proj + (long long)h * D * D;
-    for (int k = lane; k < g.n; k += 64) {
-      float acc = 0.f;
-      for (int r = 0; r < D; ++r) acc = fmaf(f16_bits_to_f32(P[r * D + k]), xin[r], acc);
-      coords[k] = acc;
+    // The wave reads all of P_h (128 x 128 binary16, 32 KiB) in one round
+    // trip: load i of lane l is row 4i + l/16, columns 8(l%16) .. +8.  Each
+    // lane sums its 8 columns over its 32 rows; the four lanes holding the
+    // same columns (l, l^16, l^32, l^48) then add their sums.
+    const u32x4 *P4 = reinterpret_cast<const u32x4 *>(p.proj + (long long)h * D * D);
+    u32x4 pv[D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) pv[i] = P4[64 * i + lane];
+    const int rsub = lane >> 4, c0 = 8 * (lane & 15);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const float xr = xin[4 * i + rsub];
+      const uint32_t wv[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(f16_bits_to_f32((uint16_t)(wv[e] & 0xFFFFu)), xr, acc[2 * e]);
+        acc[2 * e + 1] = fmaf(f16_bits_to_f32((uint16_t)(wv[e] >> 16)), xr, acc[2 * e + 1]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[e] += __shfl_xor(acc[e], 16, 64);
+      acc[e] += __shfl_xor(acc[e], 32, 64);
+    }
+    if (rsub == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) coords[c0 + e] = acc[e];
     }
   }
   wave_sync();
 
+  const HeadGeom g = head_geom(p, b, h);
   uint8_t *row_codes = p.codes + g.codes_off;
   const int fam = codec_family(g.codec);
   const int bits = codec_bits(g.codec);
-  // block scale (and min), one lane per block (blocks of min(32, rank))
-  if (lane < g.nblk) {
-    const float *blk = coords + lane * g.L;
-    const long long so = g.scales_off + (long long)t * g.nblk + lane;
-    if (fam == FAM_0) {
-      float amax = 0.f;
-      for (int e = 0; e < g.L; ++e) amax = fmaxf(amax, fabsf(blk[e]));
-      const float qmax = (float)((1 << (bits - 1)) - 1);
-      uint16_t dh = f32_to_f16_bits(amax / qmax);
-      p.scales[so] = dh;
-      s_scale[lane] = f16_bits_to_f32(dh);
-    } else {
-      float lo = blk[0], hi = blk[0];
-      for (int e = 1; e < g.L; ++e) {
-        lo = fminf(lo, blk[e]);
-        hi = fmaxf(hi, blk[e]);
-      }
-      uint16_t mh = f32_to_f16_bits(lo);
-      const float m = f16_bits_to_f32(mh);
-      const float R = hi - m;
-      const float levels = (float)((1 << bits) - 1);
-      uint16_t dh = f32_to_f16_bits(R / levels);
+  // lane l holds stored coordinates 2l, 2l+1; block j (L = min(32, rank)
+  // coordinates) is lanes [j L/2, (j+1) L/2), reduced by shuffles within
+  // those aligned lane groups
+  const bool act = 2 * lane < g.n;
+  const float v0 = act ? coords[2 * lane] : 0.f, v1 = act ? coords[2 * lane + 1] : 0.f;
+  const int half = g.L / 2;
+  const int j = lane / half, lead = j * half;
+  float d = 0.f, m = 0.f;
+  if (fam == FAM_0) {
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    for (int o = half / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    const uint16_t dh = f32_to_f16_bits(amax / qmax);
+    if (act && lane == lead) p.scales[g.scales_off + (long long)t * g.nblk + j] = dh;
+    d = f16_bits_to_f32(dh);
+  } else {
+    float lo = act ? fminf(v0, v1) : __builtin_huge_valf(), hi = act ? fmaxf(v0, v1) : -__builtin_huge_valf();
+    for (int o = half / 2; o > 0; o >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    const uint16_t mh = f32_to_f16_bits(lo);
+    m = f16_bits_to_f32(mh);
+    const float levels = (float)((1 << bits) - 1);
+    const uint16_t dh = f32_to_f16_bits((hi - m) / levels);
+    if (act && lane == lead) {
+      const long long so = g.scales_off + (long long)t * g.nblk + j;
       p.scales[so] = dh;
       p.mins[so] = mh;
-      s_scale[lane] = f16_bits_to_f32(dh);
-      s_min[lane] = m;
+    }
+    d = f16_bits_to_f32(dh);
+  }
+
+  // codes of the lane's two coordinates, OR-ed into the packed row in LDS
+  // (code e at bits [e b, e b + b) of the row)
+  uint32_t *pk = reinterpret_cast<uint32_t *>(codes);       // 128 bytes: the widest row
+  if (lane < D / 4) pk[lane] = 0u;
+  wave_sync();
+  if (act) {
+    const uint32_t mask = (1u << bits) - 1u;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float x = k ? v1 : v0;
+      int q = 0;
+      if (fam == FAM_0) {
+        const float qmax = (float)((1 << (bits - 1)) - 1);
+        if (d != 0.f) q = (int)fminf(fmaxf(rintf(x / d), -qmax), qmax);
+      } else {
+        const float levels = (float)((1 << bits) - 1);
+        const float y = x - m;
+        if (d != 0.f) q = (int)fminf(fmaxf(rintf(y / d), 0.f), levels);
+      }
+      const uint32_t v = (uint32_t)q & mask;
+      const int bit = (2 * lane + k) * bits, wd = bit >> 5, sh = bit & 31;
+      __hip_atomic_fetch_or(pk + wd, v << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+      if (sh + bits > 32)
+        __hip_atomic_fetch_or(pk + wd + 1, v >> (32 - sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     }
   }
   wave_sync();
 
-  // codes (masked to `bits` bits)
-  const uint32_t mask = (1u << bits) - 1u;
-  for (int e = lane; e < g.n; e += 64) {
-    const int j = e / g.L;
-    const float d = s_scale[j];
-    int q = 0;
-    if (fam == FAM_0) {
-      const float qmax = (float)((1 << (bits - 1)) - 1);
-      if (d != 0.f) q = (int)fminf(fmaxf(rintf(coords[e] / d), -qmax), qmax);
-    } else {
-      const float levels = (float)((1 << bits) - 1);
-      const float y = coords[e] - s_min[j];
-      if (d != 0.f) q = (int)fminf(fmaxf(rintf(y / d), 0.f), levels);
-    }
-    codes[e] = (uint8_t)((uint32_t)q & mask);
-  }
-  wave_sync();
-
-  // pack: unit u (us bytes) holds row bits [8*us*u, 8*us*(u+1))
+  // store: unit u (us bytes) is bytes [us u, us (u+1)) of the packed row
   const int us = g.c < 4 ? g.c : 4;
   const int nunits = g.R / us;
   if (lane < nunits) {
-    const int bit0 = 8 * us * lane, bit1 = bit0 + 8 * us;
-    uint64_t acc = 0;
-    for (int e = bit0 / bits; e < g.n && e * bits < bit1; ++e) {
-      const int sh = e * bits - bit0;
-      const uint64_t v = codes[e];
-      acc |= sh >= 0 ? (v << sh) : (v >> (-sh));
-    }
     const int byte = us * lane;
     uint8_t *dst = row_codes + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c;
     if (us == 4)
-      *reinterpret_cast<uint32_t *>(dst) = (uint32_t)acc;
+      *reinterpret_cast<uint32_t *>(dst) = pk[lane];
     else if (us == 2)
-      *reinterpret_cast<uint16_t *>(dst) = (uint16_t)acc;
+      *reinterpret_cast<uint16_t *>(dst) = reinterpret_cast<const uint16_t *>(pk)[lane];
     else
-      *dst = (uint8_t)acc;
+      *dst = reinterpret_cast<const uint8_t *>(pk)[lane];
   }
+  }  // LR
 }
 
 // Every wave takes a contiguous run of items (consecutive new tokens of one
@@ -181,6 +212,9 @@ __device__ __forceinline__ void append_item(const PlaneArgs &p, int n_new, int t
 // far fewer workgroups than items for a prefill-sized append.
 constexpr int AP_WAVES = 8;
 
+// LR: the layer has low-rank planes (their projection path is compiled only
+// into this instance, which needs far more registers).
+template <bool LR>
 __global__ __launch_bounds__(64 * AP_WAVES) void append_kernel(PlaneArgs kp, PlaneArgs vp,
                                                                const float *__restrict__ k_new,
                                                                const float *__restrict__ v_new,
@@ -189,9 +223,7 @@ __global__ __launch_bounds__(64 * AP_WAVES) void append_kernel(PlaneArgs kp, Pla
                                                                unsigned items) {
   __shared__ float xin[AP_WAVES][D];
   __shared__ float coords[AP_WAVES][D];
-  __shared__ uint8_t codes[AP_WAVES][D];
-  __shared__ float s_scale[AP_WAVES][4];
-  __shared__ float s_min[AP_WAVES][4];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[AP_WAVES][D];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hkv = kp.hkv;
   const unsigned waves = gridDim.x * (unsigned)AP_WAVES;
@@ -223,9 +255,9 @@ __global__ __launch_bounds__(64 * AP_WAVES) void append_kernel(PlaneArgs kp, Pla
     // ragged batch: sequence b appends at its own position
     const int tb = seq ? __builtin_amdgcn_readfirstlane(seq[it.b]) : t0;
     if (it.which)
-      append_item(vp, n_new, tb, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+      append_item<LR>(vp, n_new, tb, it, x, xin[w], coords[w], codes[w]);
     else
-      append_item(kp, n_new, tb, it, x, xin[w], coords[w], codes[w], s_scale[w], s_min[w]);
+      append_item<LR>(kp, n_new, tb, it, x, xin[w], coords[w], codes[w]);
     it = nx;
     x = xn;
   }
@@ -239,8 +271,12 @@ hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   long long blocks = (items + AP_WAVES - 1) / AP_WAVES;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(64 * AP_WAVES), 0, stream, kp, vp,
-                     k_new, v_new, n_new, t0, batch, seq, (unsigned)items);
+  if (kp.basis == KVQ_BASIS_LOWRANK || vp.basis == KVQ_BASIS_LOWRANK)
+    hipLaunchKernelGGL(append_kernel<true>, dim3((unsigned)blocks), dim3(64 * AP_WAVES), 0, stream, kp,
+                       vp, k_new, v_new, n_new, t0, batch, seq, (unsigned)items);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3((unsigned)blocks), dim3(64 * AP_WAVES), 0, stream, kp,
+                       vp, k_new, v_new, n_new, t0, batch, seq, (unsigned)items);
   return hipGetLastError();
 }
 

@@ -67,6 +67,12 @@ struct PlaneArgs {
   int tail_bf16;      // tail rows are bfloat16 (else binary16)
   int8_t hcodec[MAXLR];   // low-rank: codec of head h
   int16_t hrank[MAXLR];   // low-rank: width of head h
+  // low-rank: per token, row bytes and scale blocks of the heads before h,
+  // and of all heads (a plane's offsets are prefix sums over heads)
+  int32_t hrow_before[MAXLR];
+  int32_t hblk_before[MAXLR];
+  int32_t row_all;
+  int32_t blk_all;
 };
 
 struct HeadGeom {
@@ -90,23 +96,14 @@ __host__ __device__ inline HeadGeom head_geom(const PlaneArgs &p, int b, int h) 
     g.scales_off = plane * p.capacity * g.nblk;
     return g;
   }
-  long long rb_before = 0, nb_before = 0, rb_all = 0, nb_all = 0;
-  for (int i = 0; i < p.hkv; ++i) {
-    int r = p.hrank[i];
-    int rb = row_bytes(p.hcodec[i], r);
-    int nb = r / block_len(r);
-    if (i < h) { rb_before += rb; nb_before += nb; }
-    rb_all += rb;
-    nb_all += nb;
-  }
   g.codec = p.hcodec[h];
   g.n = p.hrank[h];
   g.R = row_bytes(g.codec, g.n);
   g.c = chunk_bytes(g.R);
   g.L = block_len(g.n);
   g.nblk = g.n / g.L;
-  g.codes_off = (long long)p.capacity * (b * rb_all + rb_before);
-  g.scales_off = (long long)p.capacity * (b * nb_all + nb_before);
+  g.codes_off = (long long)p.capacity * ((long long)b * p.row_all + p.hrow_before[h]);
+  g.scales_off = (long long)p.capacity * ((long long)b * p.blk_all + p.hblk_before[h]);
   return g;
 }
 

@@ -82,15 +82,21 @@ __global__ __launch_bounds__(64) void lowrank_query_kernel(const float *__restri
   const float *qrow = nullptr;
   if (ma < M) qrow = q + ((long long)(ma / G) * Hq + g * G + ma % G) * D;
 
+  // every load is issued before the products: the lane's 32 query values
+  // once, then per 16-column tile its 32 entries of P
+  float qa[D / 4];
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) qa[i] = qrow ? qrow[4 * i + k_a] : 0.f;
   float rowsum[4] = {0.f, 0.f, 0.f, 0.f};
   for (int ct = 0; ct < L / 16; ++ct) {
     const int n0 = jb * L + ct * 16;
+    uint16_t pb[D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) pb[i] = P[(long long)(4 * i + k_a) * D + n0 + i_a];
     floatx4 c = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const float av = qrow ? qrow[k0 + k_a] : 0.f;
-      const float bv = f16_bits_to_f32(P[(long long)(k0 + k_a) * D + n0 + i_a]);
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, c, 0, 0, 0);
-    }
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i], f16_bits_to_f32(pb[i]), c, 0, 0, 0);
     // D[i][j]: lane holds rows 4*(lane/16) + rr, column lane % 16
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {

@@ -801,14 +801,6 @@ __device__ __forceinline__ int lr_codec(int h) {
 }
 // Geometry of low-rank plane (b, h): offsets are prefix sums over heads.
 __device__ __forceinline__ HeadGeom lr_geom(const DecodeArgs &a, int b, int h) {
-  long long rb_before = 0, nb_before = 0, rb_all = 0, nb_all = 0;
-  for (int i = 0; i < a.Hkv; ++i) {
-    const int r = lr_rank(i), c = lr_codec(i);
-    const int rb = row_bytes(c, r), nb = r / block_len(r);
-    if (i < h) { rb_before += rb; nb_before += nb; }
-    rb_all += rb;
-    nb_all += nb;
-  }
   HeadGeom g;
   g.codec = lr_codec(h);
   g.n = lr_rank(h);
@@ -816,8 +808,10 @@ __device__ __forceinline__ HeadGeom lr_geom(const DecodeArgs &a, int b, int h) {
   g.c = chunk_bytes(g.R);
   g.L = block_len(g.n);
   g.nblk = g.n / g.L;
-  g.codes_off = (long long)a.k.capacity * (b * rb_all + rb_before);
-  g.scales_off = (long long)a.k.capacity * (b * nb_all + nb_before);
+  const int rb = decode_arg_at<int32_t>(offsetof(DecodeArgs, k) + offsetof(PlaneArgs, hrow_before), h);
+  const int nb = decode_arg_at<int32_t>(offsetof(DecodeArgs, k) + offsetof(PlaneArgs, hblk_before), h);
+  g.codes_off = (long long)a.k.capacity * ((long long)b * a.k.row_all + rb);
+  g.scales_off = (long long)a.k.capacity * ((long long)b * a.k.blk_all + nb);
   return g;
 }
 
