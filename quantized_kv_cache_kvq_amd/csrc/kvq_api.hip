@@ -453,7 +453,9 @@ kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, fl
     P.S_body = 0;
   }
   P.S_total = P.S_body + P.S_tail;
-  P.prep = L.k.basis != KVQ_BASIS_PLAIN || codec_family(L.k.codec) == FAM_1;
+  // plain bodies need no query pre-transform (the kernel scales the raw
+  // query itself); KVarN bodies need the rotation
+  P.prep = L.k.basis == KVQ_BASIS_HADAMARD;
   P.qsum = true;
 
   const WsLayout W = ws_layout(L, n_q_heads, P.S_total);

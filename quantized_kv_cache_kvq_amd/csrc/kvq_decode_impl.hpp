@@ -28,6 +28,11 @@ namespace kvq {
 namespace kvq {
 
 constexpr int NWAVE = DECODE_WG_WAVES;
+// Splits with at least this many tiles per wave hand tiles out at run time
+// (the second wave of each SIMD gets its first tile several microseconds
+// after the first; with a few tiles per wave a static round-robin is as
+// fast and keeps the result independent of timing).
+constexpr int DYN_TILES_PER_WAVE = 4;
 constexpr int WG = 64 * NWAVE;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_huge_valf();
@@ -346,6 +351,7 @@ struct SplitIO {
   long long t_begin, t_end;    // token range (plane coordinates), t_begin % 64 == 0
   float *part;                 // partial row of head 0 of the group
   long long part_head_stride;  // floats between consecutive heads' partials
+  int dyn;                     // integer path: waves claim tiles past their first at run time
 };
 
 __device__ __forceinline__ uint2 side_raw(const uint16_t *base, long long t, bool valid, int nb) {
@@ -858,6 +864,7 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, in
   }
   io.part = a.part + (((long long)b * a.Hq + head0) * a.S_total + s) * PSTRIDE;
   io.part_head_stride = (long long)a.S_total * PSTRIDE;
+  io.dyn = a.tps_body >= DYN_TILES_PER_WAVE * NWAVE;
   if constexpr (BodyLds<C>::INT_QK) attend_q<C>(io, lds);
   else attend_range<C>(io, lds);
 }

@@ -173,6 +173,16 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   uint8_t *vlds = wl;                                              // [TT][VPITCH]
   uint8_t *alds = wl + Q::W_V;                                     // [NBV][TT][16] f16
 
+  // run-time tiles: every wave takes its first tile by index, then claims
+  // the next unclaimed one from a workgroup counter each time it starts a
+  // tile, so waves whose data arrive first take more tiles (the counter is
+  // set while the waves still enter together)
+  __shared__ int tile_ctr;
+  if (io.dyn) {
+    if (tid == 0) tile_ctr = 0;
+    __syncthreads();
+  }
+
   // the query rows this lane digitises (loaded before the tile loads so
   // that waiting for them does not wait for the tile)
   float qraw[HGRP][NKB][8];
@@ -194,13 +204,14 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     }
   }
 
-  // ---- tiles of this wave: t_begin / TT + wave + NWAVE * i (tile indices;
-  // the loop carries the tile index, which keeps fewer values live than a
-  // token counter); 32-bit in-plane offsets; tokens past t_end load token
-  // t_end - 1 (masked later)
+  // ---- tiles of this wave: t_begin / TT + wave, then every NWAVE-th (or,
+  // for long splits, the ones it claims; tile indices: the loop carries the
+  // tile index, which keeps fewer values live than a token counter); 32-bit
+  // in-plane offsets; tokens past t_end load token t_end - 1 (masked later)
   const int t_end = (int)io.t_end;
   const int lim_tiles = (t_end + TT - 1) / TT;
-  int cur = (int)(io.t_begin / TT) + wave;
+  const int tile0 = (int)(io.t_begin / TT);
+  int cur = tile0 + wave;
 
   uint64_t kr[NT][NKB];
   uint2 ksr[NT], kmr[NT], vsr[NT], vmr[NT];
@@ -338,7 +349,13 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   }
 
   while (cur < lim_tiles) {
-    const int nxt = cur + NWAVE;
+    int nxt = cur + NWAVE;
+    if (io.dyn) {
+      int claim = 0;
+      if (lane == 0)
+        claim = __hip_atomic_fetch_add(&tile_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      nxt = tile0 + NWAVE + __builtin_amdgcn_readfirstlane(claim);
+    }
     const bool more = nxt < lim_tiles;
     const int t0 = cur * TT;
     const int tn = more ? nxt * TT : t0;               // prefetch target
