@@ -132,3 +132,36 @@ def test_append_is_deterministic(gpu):
         _append_chunks(cache, k, v, [256], gpu)
         outs.append(H.download(cache, "k")["codes"])
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_lowrank_prefill_ragged_tail(gpu):
+    """A prefill-sized low-rank append (the 16-token matrix-core path) into a
+    ragged batch with a precision tail: sequence b appends n tokens at its
+    own position; codes follow the tie rule against the oracle's encoding of
+    those tokens, and the tail ring (all newest 64 from this call) is exact."""
+    Ts0, n = [0, 21, 40], 90
+    wl = synth.WORKLOADS["lowrank_1bpd"].with_(B=3, T=n, N=64)
+    k = synth.layer_rows(wl, 0, "k")              # [3, n, Hkv, 128]: each sequence's new tokens
+    v = synth.layer_rows(wl, 0, "v")
+    gk, gv, ok_, ov = H.specs(wl)
+    cap = 192
+    cache = H.new_cache(wl, cap, gk, gv, gpu, N=64)
+    cache.n_tokens = max(Ts0)
+    cache.set_seq_tokens(torch.tensor(Ts0, dtype=torch.int32, device=gpu))
+    cache.append(k.to(gpu), v.to(gpu))
+    torch.cuda.synchronize()
+    assert cache.seq_tokens.cpu().tolist() == [t + n for t in Ts0]
+    for name, x, spec in (("k", k.numpy(), ok_), ("v", v.numpy(), ov)):
+        encs, buf = H.unpack(cache, name, spec, max(Ts0) + n)
+        for b in range(3):
+            for h in range(wl.Hkv):
+                e = encs[b][h]
+                rows = {key: (val[Ts0[b]:Ts0[b] + n] if val is not None else None) for key, val in e.items()}
+                H.check_rotated_head(x[b, :, h, :], rows, spec, h)
+        # sequence b's tokens sit at positions Ts0[b] ..; n >= 64, so every
+        # ring slot holds one of this call's tokens
+        rings = []
+        for b in range(3):
+            xb = np.concatenate([np.zeros((1, Ts0[b], wl.Hkv, 128), np.float32), x[b:b + 1]], axis=1)
+            rings.append(OL.tail_ring(xb, 64))
+        assert np.array_equal(buf["tail"], OL.pack_tail(np.concatenate(rings))), name
