@@ -378,13 +378,17 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
         } else if constexpr (VB == 1) {
           w = (vw[G / 4] >> (8 * (G & 3))) & 0xFFu;
         } else {
-          // VB bytes starting at byte VB * G of the row
+          // VB bytes starting at byte VB * G of the row: funnel shifts over
+          // the (at most three) words they touch, on named words (a 64-bit
+          // read across the word array kept it in scratch for 5 and 6 bits)
           const int bit = 8 * VB * G;
           const int wi = bit >> 5, sh = bit & 31;
-          uint64_t lo = (uint64_t)vw[wi] | ((wi + 1 < VW ? (uint64_t)vw[wi + 1] : 0) << 32);
-          if (sh + 8 * VB > 64 && wi + 2 < VW) lo = (lo >> sh) | ((uint64_t)vw[wi + 2] << (64 - sh));
-          else lo >>= sh;
-          w = lo;
+          const uint32_t w0 = vw[wi];
+          const uint32_t w1 = wi + 1 < VW ? vw[wi + 1] : 0u;
+          const uint32_t w2 = wi + 2 < VW ? vw[wi + 2] : 0u;
+          const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)sh);
+          const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, (uint32_t)sh);
+          w = (uint64_t)lo | ((uint64_t)hi << 32);
         }
         uint2 b = group_bytes<VB, C::VFAM>(w);
         if constexpr (VB == 8 && C::VFAM == FAM_0) { b.x ^= 0x80808080u; b.y ^= 0x80808080u; }
