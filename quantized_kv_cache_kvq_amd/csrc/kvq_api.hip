@@ -181,6 +181,18 @@ constexpr int TAIL_TILES_PER_SPLIT = DECODE_WG_WAVES;
 // MI355X).
 constexpr double PLAN_TILE_COST = 16384.0;
 
+// Relative decode time of a low-rank head's body per tile, by bits (1..4)
+// and rank (16, 32, 64, 128): measured on MI355X as the kernel time of a
+// layer whose eight heads all share that (rank, bits), 8 sequences of 64k
+// tokens, less the fixed per-launch part.  Other pairs: rank-proportional.
+double lowrank_tile_cost(int codec, int rank) {
+  static const double cost[4][4] = {{70, 37, 59, 113}, {36, 39, 62, 119}, {81, 49, 87, 175}, {78, 38, 61, 129}};
+  const int bits = codec_bits(codec);
+  const int ri = rank == 16 ? 0 : rank == 32 ? 1 : rank == 64 ? 2 : rank == 128 ? 3 : -1;
+  if (codec_family(codec) == FAM_1 && bits >= 1 && bits <= 4 && ri >= 0) return cost[bits - 1][ri];
+  return 30.0 + 0.7 * rank;
+}
+
 // Body bytes per token of a layer (codes, scales, mins of K and V; the mean
 // over kv heads for low rank).
 double body_token_bytes(const kvq_layer &L) {
@@ -452,6 +464,55 @@ kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, fl
     P.tiles_per_split_body = 1;
     P.S_body = 0;
   }
+  // Low rank: a tile's decode time depends on the head's (rank, bits), so
+  // the body workgroups of a batch entry are shared out over its kv heads in
+  // proportion to that time (largest remainder); explicit body_splits keep
+  // one count for every head.
+  int16_t lr_sb[KVQ_MAX_LOWRANK_HEADS] = {0}, lr_tp[KVQ_MAX_LOWRANK_HEADS] = {0};
+  if (L.k.basis == KVQ_BASIS_LOWRANK && body_tiles > 0) {
+    const int H = L.n_kv_heads;
+    int sh[KVQ_MAX_LOWRANK_HEADS];
+    if (body_splits > 0) {
+      for (int h = 0; h < H; ++h) sh[h] = P.S_body;
+    } else {
+      int slots = (DECODE_WG_PER_CU * device_cus()) / (P.B * P.NHG) - H * P.S_tail;
+      if (slots < H) slots = H;
+      double w[KVQ_MAX_LOWRANK_HEADS], frac[KVQ_MAX_LOWRANK_HEADS], sum = 0.0;
+      for (int h = 0; h < H; ++h) sum += (w[h] = lowrank_tile_cost(L.k.head_codec[h], L.k.rank[h]));
+      int used = 0;
+      for (int h = 0; h < H; ++h) {
+        const double e = slots * w[h] / sum;
+        sh[h] = (int)e;
+        frac[h] = e - sh[h];
+        if (sh[h] < 1) {
+          sh[h] = 1;
+          frac[h] = -1.0;
+        }
+        used += sh[h];
+      }
+      while (used < slots) {
+        int best = -1;
+        for (int h = 0; h < H; ++h)
+          if (frac[h] >= 0.0 && (best < 0 || frac[h] > frac[best])) best = h;
+        if (best < 0) break;
+        ++sh[best];
+        frac[best] = -1.0;
+        ++used;
+      }
+    }
+    int smax = 1;
+    for (int h = 0; h < H; ++h) {
+      int want = sh[h];
+      if (want > MAX_BODY_SPLITS) want = MAX_BODY_SPLITS;
+      if (want > body_tiles) want = body_tiles;
+      if (want < 1) want = 1;
+      const int tps = (body_tiles + want - 1) / want;
+      lr_tp[h] = (int16_t)tps;
+      lr_sb[h] = (int16_t)((body_tiles + tps - 1) / tps);
+      if (lr_sb[h] > smax) smax = lr_sb[h];
+    }
+    P.S_body = smax;
+  }
   P.S_total = P.S_body + P.S_tail;
   // plain bodies need no query pre-transform (the kernel scales the raw
   // query itself); KVarN bodies need the rotation
@@ -496,6 +557,13 @@ kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, fl
   a.tps_body = P.tiles_per_split_body;
   a.tps_tail = P.tiles_per_split_tail;
   a.tt_body = P.tt_body;
+  a.lr_body_all = 0;
+  for (int h = 0; h < KVQ_MAX_LOWRANK_HEADS; ++h) {
+    a.lr_sbody[h] = lr_sb[h];
+    a.lr_tps[h] = lr_tp[h];
+    a.lr_first[h] = (int16_t)a.lr_body_all;
+    if (h < L.n_kv_heads) a.lr_body_all += lr_sb[h];
+  }
   hipError_t e = launch_decode(a, q, sm_scale, reinterpret_cast<float *>(wsb + W.qw),
                                reinterpret_cast<float *>(wsb + W.qsum), out,
                                reinterpret_cast<hipStream_t>(stream), P.prep, P.qsum);

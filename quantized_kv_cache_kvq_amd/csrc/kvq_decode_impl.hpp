@@ -343,6 +343,12 @@ __device__ __forceinline__ half8 k_convert(const KRaw<C> &r) {
 
 // ------------------------------------------------------- one split range --
 
+// Split counts of one unit: body splits, tail splits, body tiles per split.
+// Uniform over units for fixed-codec layers; per kv head for low rank.
+struct Splits {
+  int sb, st, tps;
+};
+
 struct SplitIO {
   const uint8_t *kcodes; const uint16_t *ksc; const uint16_t *kmn;
   const uint8_t *vcodes; const uint16_t *vsc; const uint16_t *vmn;
@@ -805,6 +811,9 @@ __device__ __forceinline__ int lr_rank(int h) {
 __device__ __forceinline__ int lr_codec(int h) {
   return decode_arg_at<int8_t>(offsetof(DecodeArgs, k) + offsetof(PlaneArgs, hcodec), h);
 }
+__device__ __forceinline__ int lr_sbody(int h) { return decode_arg_at<int16_t>(offsetof(DecodeArgs, lr_sbody), h); }
+__device__ __forceinline__ int lr_tps(int h) { return decode_arg_at<int16_t>(offsetof(DecodeArgs, lr_tps), h); }
+__device__ __forceinline__ int lr_first(int h) { return decode_arg_at<int16_t>(offsetof(DecodeArgs, lr_first), h); }
 // Geometry of low-rank plane (b, h): offsets are prefix sums over heads.
 __device__ __forceinline__ HeadGeom lr_geom(const DecodeArgs &a, int b, int h) {
   HeadGeom g;
@@ -833,7 +842,8 @@ __device__ __forceinline__ void seq_counts(const DecodeArgs &a, int b, int &body
 // LR: per-head widths and codecs (low-rank planes, offsets from the head
 // tables); otherwise every plane has the configuration's fixed geometry.
 template <class C, bool LR>
-__device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
+__device__ __forceinline__ void run_body(const DecodeArgs &a, const Splits &sp, int b, int kvh, int hg, int s,
+                                         uint8_t *lds) {
   long long kco, kso, vco, vso;
   if constexpr (LR) {
     const HeadGeom gk = lr_geom(a, b, kvh), gv = gk;
@@ -854,7 +864,7 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, in
   io.vmn = a.v.mins ? a.v.mins + vso : nullptr;
   io.q = a.q_body + ((long long)b * a.Hq + head0) * D;
   io.scale = a.scale_body;
-  const long long tps = (long long)a.tps_body * 64;
+  const long long tps = (long long)sp.tps * 64;
   io.t_begin = (long long)s * tps;
   io.t_end = io.t_begin + tps < a.body_tokens ? io.t_begin + tps : a.body_tokens;
   if (a.seq) {
@@ -864,17 +874,18 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, int b, int kvh, in
   }
   io.part = a.part + (((long long)b * a.Hq + head0) * a.S_total + s) * PSTRIDE;
   io.part_head_stride = (long long)a.S_total * PSTRIDE;
-  io.dyn = a.tps_body >= DYN_TILES_PER_WAVE * NWAVE;
+  io.dyn = sp.tps >= DYN_TILES_PER_WAVE * NWAVE;
   if constexpr (BodyLds<C>::INT_QK) attend_q<C>(io, lds);
   else attend_range<C>(io, lds);
 }
 
 template <int HG, bool BF>
-__device__ __forceinline__ void run_tail(const DecodeArgs &a, int b, int kvh, int hg, int s, uint8_t *lds) {
+__device__ __forceinline__ void run_tail(const DecodeArgs &a, const Splits &sp, int b, int kvh, int hg, int s,
+                                         uint8_t *lds) {
   using C = Cfg<HG, KVQ_F16, KVQ_F16, D, D>;
   const long long plane = (long long)b * a.Hkv + kvh;
   const int head0 = kvh * a.G + hg * HG;
-  const int st = s - a.S_body;
+  const int st = s - sp.sb;
   SplitIO io;
   io.kcodes = reinterpret_cast<const uint8_t *>(a.k.tail) + plane * a.k.tail_len * (2 * D);
   io.vcodes = reinterpret_cast<const uint8_t *>(a.v.tail) + plane * a.v.tail_len * (2 * D);
@@ -903,12 +914,12 @@ __device__ __forceinline__ void run_tail(const DecodeArgs &a, int b, int kvh, in
 // are in the stored basis and go back to the raw basis first (Hadamard
 // transform and 1/w for KVarN, P_h for low rank) before they meet the tail
 // partials.  `olow` holds 128 floats of LDS.
-__device__ __forceinline__ void combine_head(const DecodeArgs &a, float *__restrict__ out, int b, int h,
-                                    float *olow) {
+__device__ __forceinline__ void combine_head(const DecodeArgs &a, const Splits &sp, float *__restrict__ out,
+                                             int b, int h, float *olow) {
   const int lane = threadIdx.x & 63;
   const long long bh = (long long)b * a.Hq + h;
   const float *pr = a.part + bh * a.S_total * PSTRIDE;
-  const int S = a.S_total, Sb = a.S_body;
+  const int S = sp.sb + sp.st, Sb = sp.sb;
 
   // Batches of up to 32 splits: every (m, l) and output load of a batch is
   // issued before any of it is used (one round trip to the coherent level
@@ -1010,19 +1021,20 @@ __device__ __forceinline__ void combine_head(const DecodeArgs &a, float *__restr
 // device-scope counter per unit in the workspace); the workgroup that
 // finishes its unit last merges the unit's heads (wave w takes head w of
 // the group) and re-arms the counter, so counters are zero between calls.
-__device__ __forceinline__ void finish_split(const DecodeArgs &a, int b, int kvh, int hg, uint8_t *lds) {
+__device__ __forceinline__ void finish_split(const DecodeArgs &a, const Splits &sp, int b, int kvh, int hg,
+                                             uint8_t *lds) {
   __shared__ unsigned s_last;
   __builtin_amdgcn_s_waitcnt(0);           // this thread's partial stores completed
   __syncthreads();
   unsigned *cnt = a.cnt + ((long long)b * a.Hkv + kvh) * a.NHG + hg;
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(a.S_total - 1);
+             (unsigned)(sp.sb + sp.st - 1);
   __syncthreads();
   if (!s_last) return;
   const int w = threadIdx.x >> 6;
   if (w < a.HG)
-    combine_head(a, a.out, b, kvh * a.G + hg * a.HG + w, reinterpret_cast<float *>(lds) + w * D);
+    combine_head(a, sp, a.out, b, kvh * a.G + hg * a.HG + w, reinterpret_cast<float *>(lds) + w * D);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1099,14 +1111,15 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs
   __shared__ __attribute__((aligned(16))) uint8_t lds[cmax<BodyLds<CB>::bytes, CT::LDS_BYTES>::value];
   int b, kvh, hg, s;
   fetch_args(a);
+  const Splits sp = {a.S_body, a.S_tail, a.tps_body};
   const bool tail = split_decode(a, b, kvh, hg, s);
   if (a.k_new) fused_append<KC, VC>(a, b, kvh, s, tail, lds);
   if (tail) {
-    if (a.k.tail_bf16) run_tail<HG, true>(a, b, kvh, hg, s, lds);
-    else run_tail<HG, false>(a, b, kvh, hg, s, lds);
+    if (a.k.tail_bf16) run_tail<HG, true>(a, sp, b, kvh, hg, s, lds);
+    else run_tail<HG, false>(a, sp, b, kvh, hg, s, lds);
   }
-  else run_body<CB, false>(a, b, kvh, hg, s, lds);
-  finish_split(a, b, kvh, hg, lds);
+  else run_body<CB, false>(a, sp, b, kvh, hg, s, lds);
+  finish_split(a, sp, b, kvh, hg, lds);
 }
 
 // Low-rank body: per-head (codec, rank) chosen at run time among the
@@ -1127,19 +1140,34 @@ struct LrLds {
 template <int HG>
 __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[LrLds<HG>::bytes];
-  int b, kvh, hg, s;
   fetch_args(a);
-  if (split_decode(a, b, kvh, hg, s)) {
-    if (a.k.tail_bf16) run_tail<HG, true>(a, b, kvh, hg, s, lds);
-    else run_tail<HG, false>(a, b, kvh, hg, s, lds);
+  // Per-head split counts (a head's tiles cost more or less with its rank
+  // and bits).  Grid x runs over every (kv head, split) of one batch entry
+  // and head group: the body splits head by head (head h's first at
+  // lr_first[h]), then S_tail tail splits per head; y = head group, z =
+  // batch entry.
+  const int x = (int)blockIdx.x, hg = (int)blockIdx.y, b = (int)blockIdx.z;
+  const bool tail = x >= a.lr_body_all;
+  int kvh = 0;
+  if (!tail) {
+    for (int h = 1; h < a.Hkv; ++h)
+      if (x >= lr_first(h)) kvh = h;
+  } else {
+    kvh = (x - a.lr_body_all) / a.S_tail;
+  }
+  const Splits sp = {lr_sbody(kvh), a.S_tail, lr_tps(kvh)};
+  const int s = tail ? sp.sb + (x - a.lr_body_all - kvh * a.S_tail) : x - lr_first(kvh);
+  if (tail) {
+    if (a.k.tail_bf16) run_tail<HG, true>(a, sp, b, kvh, hg, s, lds);
+    else run_tail<HG, false>(a, sp, b, kvh, hg, s, lds);
   } else {
     const int codec = lr_codec(kvh), rank = lr_rank(kvh);
 #define KVQ_LR_DISPATCH(CC, RR)                                                           \
-    if (codec == CC && rank == RR) run_body<Cfg<HG, CC, CC, RR, RR>, true>(a, b, kvh, hg, s, lds); else
+    if (codec == CC && rank == RR) run_body<Cfg<HG, CC, CC, RR, RR>, true>(a, sp, b, kvh, hg, s, lds); else
     KVQ_LR_CASES(KVQ_LR_DISPATCH) {}
 #undef KVQ_LR_DISPATCH
   }
-  finish_split(a, b, kvh, hg, lds);
+  finish_split(a, sp, b, kvh, hg, lds);
 }
 
 inline bool decode_lowrank_supported_impl(int codec, int rank) {
@@ -1164,7 +1192,8 @@ template <int HG>
 hipError_t launch_decode_hg(const DecodeArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const dim3 grid((unsigned)(a.S_body + a.S_tail), (unsigned)(a.Hkv * a.NHG), (unsigned)a.B);
   if (a.k.basis == KVQ_BASIS_LOWRANK) {
-    hipExtLaunchKernelGGL(decode_lowrank_kernel<HG>, grid, dim3(WG), 0, st, ev0, ev1, 0, a);
+    const dim3 lgrid((unsigned)(a.lr_body_all + a.Hkv * a.S_tail), (unsigned)a.NHG, (unsigned)a.B);
+    hipExtLaunchKernelGGL(decode_lowrank_kernel<HG>, lgrid, dim3(WG), 0, st, ev0, ev1, 0, a);
     return hipGetLastError();
   }
   const int kc = a.k.codec, vc = a.v.codec;

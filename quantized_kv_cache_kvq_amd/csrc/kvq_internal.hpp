@@ -44,6 +44,10 @@ struct DecodeArgs {
   const float *k_new;     // fused step (non-null): the new token's K and V rows
   const float *v_new;     // [B][Hkv][128], written before the decode reads
   PlaneArgs k, v;
+  int16_t lr_sbody[MAXLR];  // low rank: body splits of kv head h (S_body is the largest)
+  int16_t lr_tps[MAXLR];    // low rank: body tiles per split of kv head h
+  int16_t lr_first[MAXLR];  // low rank: grid x of kv head h's first body split
+  int lr_body_all;          // low rank: body splits of all kv heads
 };
 
 hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
