@@ -1,8 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (default split plan, one-token append after the prefix).
+benchmark times: the prefix of T - 1 tokens appended by the library, then
+one decode step through the one-call entry point (append of the last token
+and decode in the same launch, default split plan).
 
-The cache is built on the device from device-generated inputs by the
-library's own append, exactly as in a decode step.  The oracle then checks:
+Inputs are device-generated; the oracle then checks, after the step:
 
 * 32k GQA workload: every K/V code, scale and tail byte of all 8 kv heads
   bit-exact against the oracle's encoding of the same inputs, and all 32
@@ -34,16 +35,20 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
 def _build(gpu, wl, layer=0, codec=None):
-    """Device cache of one layer: append T-1 tokens, then one (a decode step)."""
+    """Device cache of one layer after one decode step: T-1 tokens appended,
+    then the one-call step (append token T-1 + decode).  Returns the step's
+    output as float64 numpy [B][Hq][128] with the cache."""
     gk, gv, ok_, ov = H.specs(wl, layer, kcodec=codec, vcodec=codec)
     capacity = (wl.T + 63) // 64 * 64
     cache = H.new_cache(wl, capacity, gk, gv, gpu)
     k = synth.layer_rows(wl, layer, "k", device=gpu)
     v = synth.layer_rows(wl, layer, "v", device=gpu)
+    q = synth.queries(wl, layer, device=gpu)
     cache.append(k[:, : wl.T - 1], v[:, : wl.T - 1])
-    cache.append(k[:, wl.T - 1:].contiguous(), v[:, wl.T - 1:].contiguous())
+    out = cache.append_decode(k[:, wl.T - 1:].contiguous(), v[:, wl.T - 1:].contiguous(), q, wl.sm_scale)
     torch.cuda.synchronize()
-    return cache, k, v, ok_, ov
+    assert cache.n_tokens == wl.T
+    return cache, k, v, ok_, ov, out.cpu().numpy().astype(np.float64), q.cpu().numpy()
 
 
 def _head_slice_offsets(spec, B, Hkv, capacity, b, h):
@@ -98,10 +103,7 @@ def _unit_outputs(wl, kenc, venc, ktail, vtail, kspec, vspec, h, qb):
     return attention.attend(qb[h * G:(h + 1) * G], K[:, None, :], V[:, None, :], wl.sm_scale)
 
 
-def _check_units(gpu, wl, cache, k, v, ok_, ov, units, rotated):
-    q = synth.queries(wl, 0, device=gpu)
-    out = cache.decode(q, wl.sm_scale).cpu().numpy().astype(np.float64)
-    qh = q.cpu().numpy()
+def _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated):
     G = wl.Hq // wl.Hkv
     worst = 0.0
     for (b, h) in units:
@@ -133,7 +135,7 @@ def _check_units(gpu, wl, cache, k, v, ok_, ov, units, rotated):
 
 def test_gqa4_32k_all_heads(gpu):
     wl = synth.WORKLOADS["gqa4_q8k_q4v_tail1024"]
-    cache, k, v, ok_, ov = _build(gpu, wl)
+    cache, k, v, ok_, ov, out, qh = _build(gpu, wl)
     kx, vx = k.cpu().numpy(), v.cpu().numpy()
     for name, x, spec in (("k", kx, ok_), ("v", vx, ov)):
         _, packed, tail = H.oracle_layer_bytes(x, spec, cache.capacity, wl.N)
@@ -142,20 +144,20 @@ def test_gqa4_32k_all_heads(gpu):
         assert np.array_equal(dev["scales"], packed["scales"]), name
         assert np.array_equal(dev["tail"], tail), name
     units = [(0, h) for h in range(wl.Hkv)]
-    _check_units(gpu, wl, cache, k, v, ok_, ov, units, rotated=False)
+    _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated=False)
 
 
 def test_kvarn_q3_64k_sampled(gpu):
     wl = synth.WORKLOADS["kvarn_q3_tail2048"]
-    cache, k, v, ok_, ov = _build(gpu, wl)
-    _check_units(gpu, wl, cache, k, v, ok_, ov, [(0, 0), (1, 5), (3, 7)], rotated=True)
+    cache, k, v, ok_, ov, out, qh = _build(gpu, wl)
+    _check_units(wl, cache, k, v, ok_, ov, out, qh, [(0, 0), (1, 5), (3, 7)], rotated=True)
 
 
 def test_lowrank_128k_sampled(gpu):
     wl = synth.WORKLOADS["lowrank_1bpd"]
-    cache, k, v, ok_, ov = _build(gpu, wl)
+    cache, k, v, ok_, ov, out, qh = _build(gpu, wl)
     # ranks 128, 16 and 32 (head 0, 3, 6 of the table)
-    _check_units(gpu, wl, cache, k, v, ok_, ov, [(0, 0), (5, 3), (7, 6)], rotated=True)
+    _check_units(wl, cache, k, v, ok_, ov, out, qh, [(0, 0), (5, 3), (7, 6)], rotated=True)
 
 
 def test_vbr_128k_layers_and_transcode(gpu):
@@ -165,11 +167,8 @@ def test_vbr_128k_layers_and_transcode(gpu):
     for layer, c in enumerate(sched):
         picked.setdefault(c, layer)
     for codec, layer in sorted(picked.items()):
-        cache, k, v, ok_, ov = _build(gpu, wl, layer, codec)
+        cache, k, v, ok_, ov, out, qh = _build(gpu, wl, layer, codec)
         wl_l = wl
-        q = synth.queries(wl, layer, device=gpu)
-        out = cache.decode(q, wl.sm_scale).cpu().numpy().astype(np.float64)
-        qh = q.cpu().numpy()
         G = wl.Hq // wl.Hkv
         for h in (0, 5):
             xk, xv = k[0, :, h, :].cpu().numpy(), v[0, :, h, :].cpu().numpy()
