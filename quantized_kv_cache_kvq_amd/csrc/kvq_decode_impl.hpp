@@ -379,6 +379,11 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(read_lane(x, 0), read_lane(x, 16)), fmaxf(read_lane(x, 32), read_lane(x, 48)));
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
+  return (read_lane(x, 0) + read_lane(x, 16)) + (read_lane(x, 32) + read_lane(x, 48));
+}
+
 // BF: the binary16 rows are bfloat16 (precision tail in bfloat16); only for
 // the all-16-bit configuration.
 template <class C, bool BF = false>
@@ -931,20 +936,17 @@ __device__ __forceinline__ void combine_head(const DecodeArgs &a, const Splits &
   for (int s0 = 0; s0 < S; s0 += NB) {
     const int cnt = S - s0 < NB ? S - s0 : NB;
     const int sl = s0 + (lane < cnt ? lane : cnt - 1);
-    const float2 ml = load2_agent(pr + (long long)sl * PSTRIDE);
+    const float *pb = pr + (long long)s0 * PSTRIDE;          // this batch's first split
+    const float2 ml = load2_agent(pb + (unsigned)((sl - s0) * PSTRIDE));
+    const float *po = pb + 4 + 2 * lane;
     float2 v[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int i = k < cnt ? k : cnt - 1;
-      v[k] = load2_agent(pr + (long long)(s0 + i) * PSTRIDE + 4 + 2 * lane);
+      const int i = k < cnt ? k : cnt - 1;                   // uniform
+      v[k] = load2_agent(po + (unsigned)(i * PSTRIDE));
     }
     const bool own = lane < cnt, body = sl < Sb;
-    float xb = own && body ? ml.x : NEG_INF, xt = own && !body ? ml.x : NEG_INF;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      xb = fmaxf(xb, __shfl_xor(xb, o, 64));
-      xt = fmaxf(xt, __shfl_xor(xt, o, 64));
-    }
+    const float xb = wave_max(own && body ? ml.x : NEG_INF), xt = wave_max(own && !body ? ml.x : NEG_INF);
     // rescale what earlier batches summed to the new segment maxima
     const float nmb = fmaxf(mb, xb), nmt = fmaxf(mt, xt);
     const float cb = mb == NEG_INF ? 0.f : exp2f(mb - nmb);
@@ -955,24 +957,19 @@ __device__ __forceinline__ void combine_head(const DecodeArgs &a, const Splits &
     mt = nmt;
     const float M = body ? mb : mt;
     const float wgt = !own || ml.x == NEG_INF ? 0.f : exp2f(ml.x - M);
-    float pl = body ? wgt * ml.y : 0.f, ql = body ? 0.f : wgt * ml.y;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      pl += __shfl_xor(pl, o, 64);
-      ql += __shfl_xor(ql, o, 64);
-    }
-    lb += pl;
-    lt += ql;
+    lb += wave_sum(body ? wgt * ml.y : 0.f);
+    lt += wave_sum(body ? 0.f : wgt * ml.y);
+    // split k's weight from lane k as a scalar operand (zero past cnt and in
+    // the other segment): straight-line FMAs, no per-split branch or LDS
+    // round trip
+    const float wbl = body ? wgt : 0.f, wtl = body ? 0.f : wgt;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const float wk = __shfl(wgt, k, 64);          // zero past cnt
-      if (s0 + k < Sb) {
-        ob0 = fmaf(wk, v[k].x, ob0);
-        ob1 = fmaf(wk, v[k].y, ob1);
-      } else {
-        ot0 = fmaf(wk, v[k].x, ot0);
-        ot1 = fmaf(wk, v[k].y, ot1);
-      }
+      const float wkb = read_lane(wbl, k), wkt = read_lane(wtl, k);
+      ob0 = fmaf(wkb, v[k].x, ob0);
+      ob1 = fmaf(wkb, v[k].y, ob1);
+      ot0 = fmaf(wkt, v[k].x, ot0);
+      ot1 = fmaf(wkt, v[k].y, ot1);
     }
   }
 
