@@ -186,7 +186,7 @@ constexpr double PLAN_TILE_COST = 16384.0;
 // layer whose eight heads all share that (rank, bits), 8 sequences of 64k
 // tokens, less the fixed per-launch part.  Other pairs: rank-proportional.
 double lowrank_tile_cost(int codec, int rank) {
-  static const double cost[4][4] = {{70, 37, 59, 113}, {36, 39, 62, 119}, {81, 49, 87, 175}, {78, 38, 61, 129}};
+  static const double cost[4][4] = {{37, 36, 58, 113}, {38, 37, 60, 116}, {52, 51, 86, 172}, {36, 38, 64, 130}};
   const int bits = codec_bits(codec);
   const int ri = rank == 16 ? 0 : rank == 32 ? 1 : rank == 64 ? 2 : rank == 128 ? 3 : -1;
   if (codec_family(codec) == FAM_1 && bits >= 1 && bits <= 4 && ri >= 0) return cost[bits - 1][ri];

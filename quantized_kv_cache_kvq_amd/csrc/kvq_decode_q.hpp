@@ -123,20 +123,25 @@ __device__ __forceinline__ uint32_t row_max_u16x2(uint32_t x) {
 template <class Q>
 __device__ __forceinline__ uint64_t kq_load(const uint8_t *__restrict__ tile, int tok, int j, int g) {
   constexpr int B = Q::KB, CK = Q::CK;
-  const int c0 = 32 * j + 8 * g;
-  if (c0 >= Q::NK) return 0;
+  // Every lane loads: a group past the row (rank 16 has two groups per
+  // token) reads the row's first group and is zeroed by a select.  A load
+  // skipped by a branch would make the compiler wait for every load in
+  // flight, the prefetched tile included, before the branches join.
+  const bool live = 32 * j + 8 * g < Q::NK;
+  const int c0 = live ? 32 * j + 8 * g : 0;
   const int b0 = c0 * B / 8;
+  uint64_t w;
   if constexpr (B == 8 || B == 4 || B == 2 || B == 1) {
     const uint8_t *p = tile + (unsigned)((b0 / CK) * (TILE * CK) + tok * CK + b0 % CK);
     if constexpr (B == 8) {
       const u32x2 v = ld_stream<u32x2>(p);
-      return (uint64_t)v.x | ((uint64_t)v.y << 32);
+      w = (uint64_t)v.x | ((uint64_t)v.y << 32);
     } else if constexpr (B == 4) {
-      return ld_stream<uint32_t>(p);
+      w = ld_stream<uint32_t>(p);
     } else if constexpr (B == 2) {
-      return ld_stream<uint16_t>(p);
+      w = ld_stream<uint16_t>(p);
     } else {
-      return ld_stream<uint8_t>(p);
+      w = ld_stream<uint8_t>(p);
     }
   } else if constexpr (CK >= 4) {
     // the two aligned words around the group's B bytes (a word never
@@ -147,17 +152,17 @@ __device__ __forceinline__ uint64_t kq_load(const uint8_t *__restrict__ tile, in
     const uint32_t d0 = ld_stream<uint32_t>(tile + (unsigned)((q0 / CK) * (TILE * CK) + tok * CK + q0 % CK));
     const uint32_t d1 = ld_stream<uint32_t>(tile + (unsigned)((q1 / CK) * (TILE * CK) + tok * CK + q1 % CK));
     const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, (uint32_t)sh);
-    return (uint64_t)lo | ((uint64_t)(d1 >> (8 * sh)) << 32);
+    w = (uint64_t)lo | ((uint64_t)(d1 >> (8 * sh)) << 32);
   } else {
-    uint64_t w = 0;
+    w = 0;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       const int b = b0 + i;
       w |= (uint64_t)ld_stream<uint8_t>(tile + (unsigned)((b / CK) * (TILE * CK) + tok * CK + b % CK))
            << (8 * i);
     }
-    return w;
   }
+  return live ? w : 0;
 }
 
 template <class C>
@@ -274,9 +279,9 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   {
     const int lt0 = cur < lim_tiles ? cur * TT : (int)io.t_begin;
     const int lim0 = cur < lim_tiles ? t_end - 1 - lt0 : 0;
+    load_v(lt0, lim0);                 // the loop's prefetch order, so waits count exactly
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) load_k_nt(lt0, lim0, nt);
-    load_v(lt0, lim0);
   }
   __builtin_amdgcn_sched_barrier(0);    // keep the tile loads ahead of the query work
 
