@@ -302,11 +302,18 @@ kvq_status kvq_cobra_allocate(const double *spectra, int32_t n_heads, const int3
  * [1, 1<<20]. */
 kvq_status kvq_timing_begin(int32_t capacity);
 kvq_status kvq_timing_end(double *total_ms, int32_t *count);
+/* Elapsed milliseconds of each pair recorded so far in the current timing
+ * session, in launch order (waits for them): ms_each[i] for i < *count,
+ * *count = min(pairs recorded, capacity).  Recording continues. */
+kvq_status kvq_timing_durations(float *ms_each, int32_t capacity, int32_t *count);
 
 const char *kvq_status_string(kvq_status status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *kvq_last_error(void);
 int32_t kvq_abi_version(void);
+/* Hash of the sources the library was built from (16 hex digits, comments
+ * and whitespace ignored; "unknown" when the build did not set it). */
+const char *kvq_source_hash(void);
 
 #ifdef __cplusplus
 }

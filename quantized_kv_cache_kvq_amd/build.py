@@ -26,6 +26,29 @@ FLAGS = [
 ]
 
 
+def source_hash():
+    """sha256 (16 hex digits) over the HIP sources and headers the library
+    is built from, with comments and whitespace removed: edits to comments
+    leave it unchanged.  Compiled into the library (kvq_source_hash) so that
+    lib.load() can refuse a library built from other sources."""
+    import hashlib
+    import re
+
+    def code(path):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        return " ".join(text.split()).encode()
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            h.update(code(os.path.join(CSRC, name)))
+    h.update(code(os.path.join(ROOT, "include", "kvq.h")))
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -37,9 +60,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src):
+def _compile(src, defines=()):
     obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + FLAGS + list(defines) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -51,8 +74,9 @@ def build(verbose=True, jobs=None):
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     objs = []
+    defs = ['-DKVQ_SOURCE_HASH="%s"' % source_hash()]
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        for src, obj, rc, err in ex.map(_compile, srcs):
+        for src, obj, rc, err in ex.map(lambda f: _compile(f, defs), srcs):
             if err.strip() and verbose:
                 print(err, file=sys.stderr)
             if rc != 0:

@@ -130,12 +130,27 @@ class LayerCache:
                 with torch.cuda.stream(stream):
                     self.seq_tokens.add_(n)
 
-    def workspace(self, n_q_heads):
+    def workspace(self, n_q_heads, stream=None):
+        """The layer's decode workspace for n_q_heads query heads (allocated
+        and zero-filled on first use, on the stream that will use it)."""
         need = lib.decode_workspace_bytes(self.desc, n_q_heads)
         if self._ws is None or self._ws.numel() < need:
-            # zero once: the library keeps its completion counters zero
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            st = stream if stream is not None else torch.cuda.current_stream(self.device)
+            if self._ws is not None:
+                # the old buffer may still be in use on its stream
+                self._ws.record_stream(st)
+            with torch.cuda.stream(st):
+                # zero once: the library keeps its completion counters zero
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
         return self._ws
+
+    def bind_step(self, k_new, v_new, q, sm_scale, out, stream=None):
+        """A decode step bound to fixed buffers: checks the arguments and
+        reserves the workspace once, then each call of the returned object
+        enqueues kvq_append_decode with the pre-built arguments and advances
+        n_tokens (and seq_tokens).  For serving loops that reuse the same
+        input and output buffers every step."""
+        return BoundStep(self, k_new, v_new, q, sm_scale, out, stream)
 
     def decode(self, q, sm_scale, out=None, body_splits=0, stream=None, ws=None):
         """q: float32 [B, Hq, 128] -> out float32 [B, Hq, 128]."""
@@ -145,7 +160,7 @@ class LayerCache:
         Hq = q.shape[1]
         if out is None:
             out = torch.empty_like(q)
-        ws = self.workspace(Hq) if ws is None else ws
+        ws = self.workspace(Hq, stream) if ws is None else ws
         lib.decode_attention(self.desc, _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(ws),
                              ws.numel(), _stream(self.device, stream), body_splits)
         return out
@@ -177,7 +192,7 @@ class LayerCache:
         Hq = q.shape[1]
         if out is None:
             out = torch.empty_like(q)
-        ws = self.workspace(Hq) if ws is None else ws
+        ws = self.workspace(Hq, stream) if ws is None else ws
         st = _stream(self.device, stream)
         lib.append_decode(self.desc, _ptr(k_new), _ptr(v_new), _ptr(q), Hq, float(sm_scale), _ptr(out),
                           _ptr(ws), ws.numel(), st)
@@ -205,3 +220,43 @@ class LayerCache:
         dst.n_tokens = self.n_tokens
         lib.transcode_layer(self.desc, dst.desc, _stream(self.device, stream))
         return dst
+
+
+class BoundStep:
+    """One layer's decode step (append the new token, attend) with every
+    argument of kvq_append_decode marshalled once.  Calling it enqueues the
+    step on the bound stream and advances the layer's token count; the
+    bound tensors must keep their storage (their contents may change)."""
+
+    def __init__(self, layer, k_new, v_new, q, sm_scale, out, stream=None):
+        B, Hkv = layer.batch, layer.n_kv_heads
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if (t.dtype != torch.float32 or not t.is_contiguous()
+                    or tuple(t.shape) != (B, 1, Hkv, 128) or t.device != layer.device):
+                raise ValueError("%s must be contiguous float32 [B, 1, Hkv, 128] on the layer's device" % name)
+        if (q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3 or q.shape[0] != B
+                or q.shape[2] != 128 or q.device != layer.device):
+            raise ValueError("q must be contiguous float32 [B, Hq, 128] on the layer's device")
+        if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be contiguous float32 shaped like q")
+        Hq = q.shape[1]
+        self.layer = layer
+        self.stream = stream if stream is not None else torch.cuda.current_stream(layer.device)
+        ws = layer.workspace(Hq, self.stream)
+        self._keep = (k_new, v_new, q, out, ws)
+        self._fn = lib.load().kvq_append_decode
+        self._args = (ctypes.byref(layer.desc), _ptr(k_new), _ptr(v_new), _ptr(q), Hq,
+                      ctypes.c_float(float(sm_scale)), _ptr(out), _ptr(ws), ws.numel(),
+                      ctypes.c_void_p(self.stream.cuda_stream))
+        self.out = out
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            lib.check(st)
+        layer = self.layer
+        layer.desc.n_tokens += 1
+        if layer.seq_tokens is not None:
+            with torch.cuda.stream(self.stream):
+                layer.seq_tokens.add_(1)
+        return self.out

@@ -253,6 +253,11 @@ extern "C" {
 
 int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
 
+#ifndef KVQ_SOURCE_HASH
+#define KVQ_SOURCE_HASH "unknown"
+#endif
+const char *kvq_source_hash(void) { return KVQ_SOURCE_HASH; }
+
 const char *kvq_last_error(void) { return g_err; }
 
 const char *kvq_status_string(kvq_status s) {
@@ -619,6 +624,15 @@ kvq_status kvq_timing_begin(int32_t capacity) {
     return fail(KVQ_ERR_INVALID_ARG, "timing capacity %d outside [1, 1<<20]", capacity);
   hipError_t e = kvq::timing_begin(capacity);
   return e == hipSuccess ? ok() : hip_fail(e, "kvq_timing_begin");
+}
+
+kvq_status kvq_timing_durations(float *ms_each, int32_t capacity, int32_t *count) {
+  if (!ms_each || !count || capacity < 0)
+    return fail(KVQ_ERR_INVALID_ARG, "ms_each and count must be non-NULL, capacity >= 0");
+  int n = 0;
+  hipError_t e = kvq::timing_durations(ms_each, capacity, &n);
+  *count = n;
+  return e == hipSuccess ? ok() : hip_fail(e, "kvq_timing_durations");
 }
 
 kvq_status kvq_timing_end(double *total_ms, int32_t *count) {

@@ -186,6 +186,21 @@ hipError_t timing_begin(int capacity) {
   return hipSuccess;
 }
 
+hipError_t timing_durations(float *ms, int capacity, int *count) {
+  Timing &T = g_timing;
+  hipError_t err = hipSuccess;
+  const int n = T.used < capacity ? T.used : capacity;
+  for (int i = 0; i < n; ++i) {
+    float x = 0.f;
+    hipError_t r = hipEventSynchronize(T.ev[2 * i + 1]);
+    if (r == hipSuccess) r = hipEventElapsedTime(&x, T.ev[2 * i], T.ev[2 * i + 1]);
+    if (r != hipSuccess && err == hipSuccess) err = r;
+    ms[i] = x;
+  }
+  *count = n;
+  return err;
+}
+
 hipError_t timing_end(double *total_ms, int *count) {
   Timing &T = g_timing;
   double sum = 0.0;

@@ -603,4 +603,12 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
       store_agent(dst + 1, L);
     }
   }
+  // low rank: the channels past the rank are zero, so the combine (which
+  // reads all 128 of every split) never meets stale workspace contents
+  if constexpr (Q::NV < D) {
+    for (int idx = tid; idx < HG * (D - Q::NV); idx += WG) {
+      const int h = idx / (D - Q::NV), c = Q::NV + idx % (D - Q::NV);
+      store_agent(io.part + h * io.part_head_stride + 4 + c, 0.f);
+    }
+  }
 }

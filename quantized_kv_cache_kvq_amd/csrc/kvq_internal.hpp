@@ -73,6 +73,8 @@ kvq_status api_ok();
 // Event timing of the split-K decode kernel (host side, not thread safe).
 hipError_t timing_begin(int capacity);
 hipError_t timing_end(double *total_ms, int *count);
+// Elapsed milliseconds of each recorded pair (at most capacity), in launch order.
+hipError_t timing_durations(float *ms, int capacity, int *count);
 // Next free event pair (nulls when timing is off or the pool is used up);
 // timing_commit() marks it used once the launch went through.
 void timing_next(hipEvent_t *ev0, hipEvent_t *ev1);

@@ -100,9 +100,12 @@ _SIGS = {
                                           ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]),
     "kvq_timing_begin": (ctypes.c_int, [ctypes.c_int32]),
     "kvq_timing_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]),
+    "kvq_timing_durations": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int32)]),
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_abi_version": (ctypes.c_int32, []),
+    "kvq_source_hash": (ctypes.c_char_p, []),
 }
 
 
@@ -121,6 +124,11 @@ def load(path=LIB_PATH):
         fn.argtypes = args
     if lib.kvq_abi_version() != 2:
         raise RuntimeError("libkvq.so ABI version mismatch")
+    from .build import source_hash
+    built, now = lib.kvq_source_hash().decode(), source_hash()
+    if built != now:
+        raise RuntimeError("libkvq.so was built from other sources (library %s, sources %s); "
+                           "rebuild with __graft_entry__.build()" % (built, now))
     _lib = lib
     return lib
 
@@ -177,6 +185,14 @@ def decode_attention(layer, q_ptr, n_q_heads, sm_scale, out_ptr, ws_ptr, ws_byte
 def timing_begin(capacity):
     """Start recording event pairs around the split-K decode kernel."""
     check(load().kvq_timing_begin(capacity))
+
+
+def timing_durations(capacity):
+    """Per-launch kernel durations (milliseconds) recorded so far."""
+    buf = (ctypes.c_float * max(1, capacity))()
+    n = ctypes.c_int32()
+    check(load().kvq_timing_durations(buf, capacity, ctypes.byref(n)))
+    return [buf[i] for i in range(n.value)]
 
 
 def timing_end():

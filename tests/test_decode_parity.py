@@ -146,3 +146,32 @@ def test_workspace_reuse_across_calls_and_shapes(gpu):
             torch.cuda.synchronize()
             err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))
             assert err <= H.ATOL, (T, N, Hq, splits, step, err)
+
+
+@pytest.mark.parametrize("N", [0, 128])
+def test_lowrank_stale_workspace(gpu, N):
+    """Only the counters at the start of a workspace must be zero: a
+    workspace whose remaining bytes hold NaN patterns (0xFF) from earlier
+    use must give the same low-rank decode, with and without a tail."""
+    wl = synth.WORKLOADS["lowrank_1bpd"].with_(B=1, T=600, N=N)
+    k = synth.layer_rows(wl, 0, "k").numpy()
+    v = synth.layer_rows(wl, 0, "v").numpy()
+    q = synth.queries(wl, 0)
+    gk, gv, ok_, ov = H.specs(wl)
+    cache = H.new_cache(wl, 640, gk, gv, gpu, N=N)
+    kenc, kp, kt = H.oracle_layer_bytes(k, ok_, 640, N)
+    venc, vp, vt = H.oracle_layer_bytes(v, ov, 640, N)
+    H.upload(cache, "k", kp, kt)
+    H.upload(cache, "v", vp, vt)
+    cache.n_tokens = wl.T
+    ref = OL.decode(q.numpy(), kenc, venc, OL.tail_ring(k, N) if N else None,
+                    OL.tail_ring(v, N) if N else None, ok_, ov, wl.T, N, wl.sm_scale)
+    need = cache.workspace(wl.Hq).numel()
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=gpu)
+    ws[: 1 << 16].zero_()
+    for splits in (0, 3):
+        out = cache.decode(q.to(gpu), wl.sm_scale, body_splits=splits, ws=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), splits
+        assert np.max(np.abs(got - ref)) <= H.ATOL, splits
