@@ -174,15 +174,18 @@ struct Cfg {
   static constexpr int TPT = 64 / TT;                        // lanes per token (staging)
   static constexpr int NGQ = (HG + 1) / 2;                   // row groups holding heads
   // LDS per wave: value rows (byte codes or binary16), weights [j][t][16
-  // rows] binary16, probabilities [h][t] fp32, per-head query scalars
+  // rows] binary16, probabilities [h][t] fp32
   static constexpr int VPITCH = VFAM == FAM_F16 ? 2 * NV + 32 : NV + 16;
   static constexpr int W_V = TT * VPITCH;
   static constexpr int W_A = NBV * TT * 32;
   static constexpr int W_P = 8 * TT * 4;
-  static constexpr int W_Q = 8 * 4 + 8 * 4 * 4;
-  static constexpr int W_BYTES = (W_V + W_A + W_P + W_Q + 15) / 16 * 16;
+  static constexpr int W_BYTES = (W_V + W_A + W_P + 15) / 16 * 16;
+  // query operands shared by the workgroup's waves: hi/lo rows
+  // [NKB][64 lanes][16 bytes], then 2^-sh [8] and block sums [8][4]
+  static constexpr int QA_OFF = NWAVE * W_BYTES;
+  static constexpr int QA_BYTES = NKB * 64 * 16 + (8 + 8 * 4) * 4;
   static constexpr int MERGE = NWAVE * HG * (NV + 4) * 4;
-  static constexpr int LDS_BYTES = cmax<NWAVE * W_BYTES, MERGE>::value;
+  static constexpr int LDS_BYTES = cmax<QA_OFF + QA_BYTES, MERGE>::value;
   static_assert(2 * HG <= 16, "at most 8 query heads per workgroup");
   static_assert(TT == 64 || VFAM == FAM_F16 || (RV / 2) % CV == 0,
                 "half-row staging needs chunk-aligned halves");
@@ -396,64 +399,9 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
   uint8_t *vlds = wl;                                               // [TT][VPITCH]
   uint8_t *alds = wl + C::W_V;                                      // [NBV][TT][16] f16
   float *plds = reinterpret_cast<float *>(wl + C::W_V + C::W_A);    // [8][TT]
-  float *qinv = plds + 8 * TT;                                      // [8]
-  float *qsum = qinv + 8;                                           // [8][4]
 
   const int n = lane & 15, g = lane >> 4;   // MFMA layout: column n, row group g
   const int tl = lane % TT, tp = lane / TT; // staging layout: token tl, row part tp
-
-  // ---- query operand: row i = lane % 16 is (head i/2, part i%2 = hi/lo)
-  half8 qa[C::NKB];
-  {
-    const int i = n, kg = g, h = i >> 1, prt = i & 1;
-    float v[C::NKB][8];
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < C::NKB; ++j) {
-      const int e0 = 32 * j + 8 * kg;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool ok = h < HG && e0 + e < C::NK;
-        v[j][e] = ok ? io.q[h * D + e0 + e] * io.scale : 0.f;
-        amax = fmaxf(amax, fabsf(v[j][e]));
-      }
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    int ex = 0;
-    if (amax > 0.f) (void)frexpf(amax, &ex);
-    const int sh = 14 - ex;                       // |q * 2^sh| < 2^14
-    const float up = ldexpf(1.f, sh);
-#pragma unroll
-    for (int j = 0; j < C::NKB; ++j) {
-      H8 a;
-      float ssum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint32_t p0 = split16<BF>(v[j][e] * up), p1 = split16<BF>(v[j][e + 1] * up);
-        a.u[e / 2] = prt ? (p0 >> 16) | (p1 & 0xFFFF0000u) : (p0 & 0xFFFFu) | (p1 << 16);
-        ssum += v[j][e];
-        ssum += v[j][e + 1];
-      }
-      qa[j] = a.h;
-      ssum += __shfl_xor(ssum, 16, 64);
-      ssum += __shfl_xor(ssum, 32, 64);
-      if (C::KFAM == FAM_1 && kg == 0 && prt == 0 && h < HG) qsum[h * 4 + j] = ssum;
-    }
-    if (kg == 0 && prt == 0 && h < HG) qinv[h] = ldexpf(1.f, -sh);
-  }
-  wave_sync_lds();
-
-  // result layout (QK and PV alike): row group g holds heads 2g (rows 4g,
-  // 4g+1: hi, lo) and 2g+1 (rows 4g+2, 4g+3)
-  float inv_k[2], qs_k[2][C::NKB];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int h = 2 * g + k;
-    inv_k[k] = h < HG ? qinv[h] : 0.f;
-#pragma unroll
-    for (int j = 0; j < C::NKB; ++j) qs_k[k][j] = (C::KFAM == FAM_1 && h < HG) ? qsum[h * 4 + j] : 0.f;
-  }
 
   float m_run[2] = {NEG_INF, NEG_INF}, l_lane[2] = {0.f, 0.f};
   float pm[NBV][2];
@@ -528,6 +476,70 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
     for (int nt = 0; nt < NT; ++nt) load_k_nt(first, nt);
     load_v(first);
   }
+
+  // ---- query operand (after the first tile's loads are out): row i = lane % 16 is (head i/2, part i%2 = hi/lo),
+  // k-group lane / 16.  Prepared once per workgroup by waves 0 and 1 (lane =
+  // (head 4w + lane/16, 8-channel group lane%16): the head's amax is a
+  // reduction over its 16-lane row) and shared through LDS.
+  uint8_t *qa_s = lds + C::QA_OFF;
+  float *qinv_s = reinterpret_cast<float *>(qa_s + C::NKB * 64 * 16);
+  float *qsum_s = qinv_s + 8;
+  if (wave < 2) {
+    const int h = 4 * wave + (lane >> 4), G = lane & 15, j = G >> 2, gk = G & 3;
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = h < HG && 8 * G + e < C::NK;
+      v[e] = ok ? io.q[h * D + 8 * G + e] * io.scale : 0.f;
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = row_max16(amax);
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);
+    const int sh = 14 - ex;                       // |q * 2^sh| < 2^14
+    const float up = ldexpf(1.f, sh);
+    H8 hi, lo;
+    float ssum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t p0 = split16<BF>(v[e] * up), p1 = split16<BF>(v[e + 1] * up);
+      hi.u[e / 2] = (p0 & 0xFFFFu) | (p1 << 16);
+      lo.u[e / 2] = (p0 >> 16) | (p1 & 0xFFFF0000u);
+      ssum += v[e];
+      ssum += v[e + 1];
+    }
+    ssum += __shfl_xor(ssum, 1, 64);
+    ssum += __shfl_xor(ssum, 2, 64);
+    if (j < C::NKB) {
+      uint4 *dst = reinterpret_cast<uint4 *>(qa_s) + j * 64 + 2 * (h & 7) + 16 * gk;
+      dst[0] = make_uint4(hi.u[0], hi.u[1], hi.u[2], hi.u[3]);
+      dst[1] = make_uint4(lo.u[0], lo.u[1], lo.u[2], lo.u[3]);
+      if (gk == 0 && h < HG) qsum_s[h * 4 + j] = ssum;
+      if (G == 0 && h < HG) qinv_s[h] = ldexpf(1.f, -sh);
+    }
+  }
+  __syncthreads();
+  half8 qa[C::NKB];
+#pragma unroll
+  for (int j = 0; j < C::NKB; ++j) {
+    H8 a;
+    const uint4 x = reinterpret_cast<const uint4 *>(qa_s)[j * 64 + lane];
+    a.u[0] = x.x; a.u[1] = x.y; a.u[2] = x.z; a.u[3] = x.w;
+    qa[j] = a.h;
+  }
+
+  // result layout (QK and PV alike): row group g holds heads 2g (rows 4g,
+  // 4g+1: hi, lo) and 2g+1 (rows 4g+2, 4g+3)
+  float inv_k[2], qs_k[2][C::NKB];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int h = 2 * g + k;
+    inv_k[k] = h < HG ? qinv_s[h] : 0.f;
+#pragma unroll
+    for (int j = 0; j < C::NKB; ++j) qs_k[k][j] = (C::KFAM == FAM_1 && h < HG) ? qsum_s[h * 4 + j] : 0.f;
+  }
+
   for (int i = lane; i < C::W_A / 16; i += 64)
     reinterpret_cast<uint4 *>(alds)[i] = make_uint4(0u, 0u, 0u, 0u);
 

@@ -99,8 +99,12 @@ struct QCfg {
   static constexpr int W_V = TT * VPITCH;
   static constexpr int W_A = NBV * TT * 32;            // [j][t][16 rows] binary16
   static constexpr int W_BYTES = (W_V + W_A + 15) / 16 * 16;
+  // query operands shared by the workgroup's waves: digit rows
+  // [HGRP][NKB][64 lanes][8 bytes], then 2^-sh [8] and block sums [8][4]
+  static constexpr int QD_OFF = NWAVE * W_BYTES;
+  static constexpr int QD_BYTES = HGRP * NKB * 64 * 8 + (8 + 8 * 4) * 4;
   static constexpr int MERGE = NWAVE * HG * (NV + 4) * 4;
-  static constexpr int LDS_BYTES = cmax<NWAVE * W_BYTES, MERGE>::value;
+  static constexpr int LDS_BYTES = cmax<QD_OFF + QD_BYTES, MERGE>::value;
   static_assert(NKB == NBK, "QK k-blocks are scale blocks");
   static_assert(KB == 1 || KB == 2 || KB == 4 || KB == 8 || KB == 3 || KB == 5 || KB == 6, "bits");
 };
@@ -188,25 +192,22 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     __syncthreads();
   }
 
-  // the query rows this lane digitises (loaded before the tile loads so
-  // that waiting for them does not wait for the tile)
-  float qraw[HGRP][NKB][8];
+  // The query operands are prepared once per workgroup by HGRP producer
+  // waves (wave rg handles row group rg: lane = (head 4rg + lane/16, 8-channel
+  // group lane%16)) and shared through LDS; the other waves only issue their
+  // tile loads and wait at one barrier.  The producers' query loads go out
+  // before their tile loads.
+  const bool producer = wave < HGRP;
+  const int ph = 4 * wave + (lane >> 4), pG = lane & 15;   // producer: head, channel group
+  float qv[8];
+  if (producer && ph < HG && 8 * pG < Q::NK) {
+    const float4 x0 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(ph * D + 8 * pG));
+    const float4 x1 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(ph * D + 8 * pG + 4));
+    qv[0] = x0.x; qv[1] = x0.y; qv[2] = x0.z; qv[3] = x0.w;
+    qv[4] = x1.x; qv[5] = x1.y; qv[6] = x1.z; qv[7] = x1.w;
+  } else {
 #pragma unroll
-  for (int rg = 0; rg < HGRP; ++rg) {
-    const int h = 4 * rg + (n >> 2);
-#pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-      const int c0 = 32 * j + 8 * g;
-      if (h < HG && c0 < Q::NK) {
-        const float4 x0 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(h * D + c0));
-        const float4 x1 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(h * D + c0 + 4));
-        qraw[rg][j][0] = x0.x; qraw[rg][j][1] = x0.y; qraw[rg][j][2] = x0.z; qraw[rg][j][3] = x0.w;
-        qraw[rg][j][4] = x1.x; qraw[rg][j][5] = x1.y; qraw[rg][j][6] = x1.z; qraw[rg][j][7] = x1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qraw[rg][j][e] = 0.f;
-      }
-    }
+    for (int e = 0; e < 8; ++e) qv[e] = 0.f;
   }
 
   // ---- tiles of this wave: t_begin / TT + wave, then every NWAVE-th (or,
@@ -285,58 +286,68 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   }
   __builtin_amdgcn_sched_barrier(0);    // keep the tile loads ahead of the query work
 
-  // ---- query digits: A row n of group rg = (head 4rg + n/4, digit n%4).
-  // Every lane also keeps 2^-sh and the block sums Q_j of head n/4; lane
-  // (n, g) of the QK result needs them for head g + 4rg (one shuffle each).
+  // ---- query digits.  A row n of group rg = (head 4rg + n/4, digit n%4):
+  // per head, q * 2^sh (|q * 2^sh| < 2^20) rounded to an integer and written
+  // as three signed base-128 digits; byte e of k-group g in block j holds
+  // channel 32j + 8g + grp8_perm(e).  A producer lane computes all digit
+  // rows of its (head, 8-channel group); the head's amax is a reduction over
+  // its 16-lane row.
+  uint64_t *qd = reinterpret_cast<uint64_t *>(lds + Q::QD_OFF);
+  float *qinv_s = reinterpret_cast<float *>(lds + Q::QD_OFF + HGRP * NKB * 64 * 8);
+  float *qsum_s = qinv_s + 8;
+  if (producer) {
+    const int hh = lane >> 4, j = pG >> 2, gk = pG & 3;
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = qv[grp8_perm<KB>(e)] * io.scale;
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+    amax = row_max16(amax);
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);
+    const int sh = 20 - ex;                         // |q * 2^sh| < 2^20
+    uint32_t w[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+    int qs = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int qi = (int)rintf(ldexpf(v[e], sh));
+      const int d2 = ((qi + 64) & 127) - 64;
+      const int r = (qi - d2) >> 7;
+      const int d1 = ((r + 64) & 127) - 64;
+      const int d0 = (r - d1) >> 7;
+      w[0][e >> 2] |= (uint32_t)(d0 & 0xFF) << (8 * (e & 3));
+      w[1][e >> 2] |= (uint32_t)(d1 & 0xFF) << (8 * (e & 3));
+      w[2][e >> 2] |= (uint32_t)(d2 & 0xFF) << (8 * (e & 3));
+      qs += qi;
+    }
+    // block sum over the 4 channel groups of block j (lanes 4j .. 4j+3 of the row)
+    qs += __shfl_xor(qs, 1, 64);
+    qs += __shfl_xor(qs, 2, 64);
+    if (j < NKB) {
+      uint64_t *dst = qd + ((wave * NKB + j) * 64 + 4 * hh + 16 * gk);
+#pragma unroll
+      for (int dg = 0; dg < 3; ++dg) dst[dg] = (uint64_t)w[dg][0] | ((uint64_t)w[dg][1] << 32);
+      dst[3] = 0ull;
+      if (gk == 0 && ph < HG) qsum_s[ph * 4 + j] = (float)qs;
+      if (pG == 0 && ph < HG) qinv_s[ph] = ldexpf(1.f, -sh);
+    }
+  }
+  __syncthreads();
+  // lane (n, g) of the QK result holds head g + 4rg
   long qA[HGRP][NKB];
   float inv[HGRP], Qb[HGRP][NKB], Qm[HGRP][NKB];
 #pragma unroll
   for (int rg = 0; rg < HGRP; ++rg) {
-    const int h = 4 * rg + (n >> 2), dg = n & 3;
-    (void)h;
-    float v[NKB][8];
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < NKB; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[j][e] = qraw[rg][j][grp8_perm<KB>(e)] * io.scale;
-        amax = fmaxf(amax, fabsf(v[j][e]));
-      }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    int ex = 0;
-    if (amax > 0.f) (void)frexpf(amax, &ex);
-    const int sh = 20 - ex;                         // |q * 2^sh| < 2^20
-    float qsj[NKB];
-#pragma unroll
-    for (int j = 0; j < NKB; ++j) {
-      uint32_t w[2] = {0u, 0u};
-      int qs = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int qi = (int)rintf(ldexpf(v[j][e], sh));
-        const int d2 = ((qi + 64) & 127) - 64;
-        const int r = (qi - d2) >> 7;
-        const int d1 = ((r + 64) & 127) - 64;
-        const int d0 = (r - d1) >> 7;
-        const int dig = (d0 & -(int)(dg == 0)) | (d1 & -(int)(dg == 1)) | (d2 & -(int)(dg == 2));
-        w[e >> 2] |= (uint32_t)(dig & 0xFF) << (8 * (e & 3));
-        qs += qi;
-      }
-      qA[rg][j] = (long)((uint64_t)w[0] | ((uint64_t)w[1] << 32));
-      qs += __shfl_xor(qs, 16, 64);
-      qs += __shfl_xor(qs, 32, 64);
-      qsj[j] = (float)qs;
-    }
-    // head g + 4rg lives in lanes 4g .. 4g+3 (any row group)
     const bool live = g + 4 * rg < HG;
-    inv[rg] = live ? __shfl(ldexpf(1.f, -sh), 4 * g, 64) : 0.f;
+    inv[rg] = live ? qinv_s[g + 4 * rg] : 0.f;
 #pragma unroll
     for (int j = 0; j < NKB; ++j) {
-      const float qs = live ? __shfl(qsj[j], 4 * g, 64) : 0.f;
-      Qb[rg][j] = (float)Q::KBIAS * qs;
-      Qm[rg][j] = qs;
+      qA[rg][j] = (long)qd[(rg * NKB + j) * 64 + lane];
+      const float qsv = live ? qsum_s[(g + 4 * rg) * 4 + j] : 0.f;
+      Qb[rg][j] = (float)Q::KBIAS * qsv;
+      Qm[rg][j] = qsv;
     }
   }
   for (int i = lane; i < Q::W_A / 16; i += 64)
