@@ -23,8 +23,12 @@ printed split, rank 16 x 4 bits and rank 96 x 2 bits (tests pin it).
 
 The allocation problem is then plainly: minimise sum_h E_h(r_h, b_h) over
 the candidate (r, b) pairs subject to sum_h r_h b_h <= budget.  The oracle
-solves it exactly by dynamic programming over the budget; the library's C1/C2
-iteration is checked against that optimum.
+solves it exactly by dynamic programming over the budget (pinned by brute
+force), bounds it from below by the continuous relaxation (weak duality),
+and writes C1 / C2 out plainly from the explainer's words (each head's best
+error at every budget; bits go where they remove the most error, then
+moves between heads until none helps).  The library's allocation is checked
+against the optimum and the relaxation, not against a copy of its loop.
 """
 
 import numpy as np
@@ -87,119 +91,135 @@ def optimum(spectra, ranks, bits, budget, gamma=GAMMA):
     return total, alloc[::-1]
 
 
-def _errors(lam, ranks, bits, gamma):
-    """Candidate list in the library's construction order (rank-major),
-    errors summed the same way (running prefix sums)."""
-    pre = [0.0]
-    for x in np.asarray(lam, np.float64):
-        pre.append(pre[-1] + float(x))
-    out = []
-    for r in ranks:
-        for b in bits:
-            q = 2.0 ** b - 1.0
-            out.append((r * b, (pre[128] - pre[r]) + gamma / (q * q) * pre[r], r, b))
-    return out
+def c1_curve(lam, ranks, bits, max_cost, gamma=GAMMA):
+    """C1 for one head, written as its definition: F(c) = the smallest error
+    of any candidate (r, b) with r*b <= c, for c = 0 .. max_cost (inf where
+    no candidate fits).  Returns (errors [max_cost+1], choice [(r, b) or
+    None])."""
+    errs = [float("inf")] * (max_cost + 1)
+    pick = [None] * (max_cost + 1)
+    for c in range(max_cost + 1):
+        for r in ranks:
+            for b in bits:
+                if r * b <= c:
+                    e = head_error(lam, r, b, gamma)
+                    if e < errs[c]:
+                        errs[c], pick[c] = e, (r, b)
+    return errs, pick
 
 
-def _hull(opts):
-    """Lower convex hull of (cost, error) over the efficient candidates."""
-    o = sorted(opts)
-    front = []
-    for x in o:
-        if not front or x[1] < front[-1][1]:
-            if front and front[-1][0] == x[0]:
-                front[-1] = x
-            else:
-                front.append(x)
-    hull = []
-    for x in front:
-        while len(hull) >= 2:
-            a, c = hull[-2], hull[-1]
-            if (c[1] - a[1]) * (x[0] - a[0]) >= (x[1] - a[1]) * (c[0] - a[0]):
-                hull.pop()
-            else:
-                break
-        hull.append(x)
-    return hull
+def _candidates(spectra, ranks, bits, gamma):
+    costs = np.array([r * b for r in ranks for b in bits], np.float64)
+    errs = np.array([[head_error(l, r, b, gamma) for r in ranks for b in bits] for l in spectra])
+    return costs, errs
 
 
-def water_fill(spectra, ranks, bits, budget, gamma=GAMMA, max_rounds=64):
-    """The C1 / C2 steps as described: C1 reduces each head to its efficient
-    (bits, error) pairs; C2 gives bits, step by step, to the head whose next
-    step removes the most error per bit, then exchanges bits between heads
-    (one head moves down, another takes the freed bits) in rounds until no
-    exchange lowers the total error.  Returns (allocation, rounds, total
-    error, fits)."""
+def lagrangian_bound(spectra, ranks, bits, budget, gamma=GAMMA):
+    """A lower bound on the optimum by weak duality: for any mu >= 0,
+    g(mu) = sum_h min_(r,b) [E_h(r, b) + mu r b] - mu * budget <= the
+    optimum.  g is concave and piecewise linear; its maximum sits at mu = 0
+    or at a mu where some head's minimiser changes, mu = (E_a - E_b) /
+    (c_b - c_a) for two candidates a, b of one head.  The sorted breakpoints
+    are searched by ternary search (g at sorted points rises, then falls).
+    Returns (max g, the maximising mu): the continuous relaxation's optimum
+    and its multiplier."""
+    costs, errs = _candidates(spectra, ranks, bits, gamma)
+    mus = [np.zeros(1)]
+    dc = costs[None, :] - costs[:, None]            # c_j - c_i
+    for e in errs:
+        de = e[:, None] - e[None, :]                # E_i - E_j
+        ok = (dc > 0) & (de > 0)
+        mus.append(de[ok] / dc[ok])
+    mus = np.unique(np.concatenate(mus))
+
+    def g(k):
+        m = mus[k]
+        return float((errs + m * costs[None, :]).min(axis=1).sum() - m * budget)
+
+    lo, hi = 0, len(mus) - 1
+    while hi - lo > 3:
+        m1, m2 = lo + (hi - lo) // 3, hi - (hi - lo) // 3
+        if g(m1) < g(m2):
+            lo = m1 + 1
+        else:
+            hi = m2
+    k = max(range(lo, hi + 1), key=g)
+    return g(k), float(mus[k])
+
+
+def rounding_gap(spectra, ranks, bits, mu, gamma=GAMMA):
+    """How far rounding the relaxation can cost: at the multiplier mu, heads
+    with several minimisers of E + mu * cost are the ones the relaxation may
+    split between two candidates; the sum over them of (largest - smallest
+    error among their minimisers).  A greedy that fills heads in order of
+    error removed per bit, stopping when the next step does not fit, ends
+    at most this far above the relaxation's optimum."""
+    costs, errs = _candidates(spectra, ranks, bits, gamma)
+    gap = 0.0
+    for e in errs:
+        val = e + mu * costs
+        m = val.min()
+        tie = np.abs(val - m) <= 1e-12 * max(1.0, abs(m)) + 1e-15
+        if tie.sum() > 1:
+            gap += float(e[tie].max() - e[tie].min())
+    return gap
+
+
+def water_fill_plain(spectra, ranks, bits, budget, gamma=GAMMA, max_rounds=50):
+    """C1 / C2 as the explainer words them.  C1: each head's best error at
+    every budget (c1_curve).  C2: start every head at its cheapest fitting
+    budget, then, while bits remain, give the next bits to the head where
+    they remove the most error per bit (any larger budget of that head that
+    fits); then, in rounds, move bits from one head to another whenever
+    that lowers the total, until a round changes nothing.  Returns
+    (allocation [(r, b)], total error, rounds) or None when even the
+    cheapest candidates exceed the budget."""
     H = len(spectra)
-    opts = [_errors(l, ranks, bits, gamma) for l in spectra]
-    hulls = [_hull(o) for o in opts]
-    pos = [0] * H
-    used = sum(h[0][0] for h in hulls)
-    if used > budget:
-        return None, 0, None, False
+    maxc = max(r * b for r in ranks for b in bits)
+    curves = [c1_curve(l, ranks, bits, maxc, gamma) for l in spectra]
+    level = []
+    for F, _ in curves:
+        c = next(c for c in range(maxc + 1) if F[c] < float("inf"))
+        level.append(c)
+    if sum(level) > budget:
+        return None
+    spare = budget - sum(level)
     while True:
-        best, gain = -1, 0.0
-        for h in range(H):
-            if pos[h] + 1 >= len(hulls[h]):
-                continue
-            a, c = hulls[h][pos[h]], hulls[h][pos[h] + 1]
-            if used + c[0] - a[0] > budget:
-                continue
-            g = (a[1] - c[1]) / float(c[0] - a[0])
-            if g > gain:
-                gain, best = g, h
-        if best < 0:
+        pick = None
+        for h, (F, _) in enumerate(curves):
+            for c in range(level[h] + 1, min(maxc, level[h] + spare) + 1):
+                gain = (F[level[h]] - F[c]) / (c - level[h])
+                if gain > 0 and (pick is None or gain > pick[0]):
+                    pick = (gain, h, c)
+        if pick is None:
             break
-        used += hulls[best][pos[best] + 1][0] - hulls[best][pos[best]][0]
-        pos[best] += 1
-    cur = [hulls[h][pos[h]] for h in range(H)]
-    # best candidate of each head at or below every cost (first of the
-    # cost-sorted list achieving the smallest error so far)
-    maxc = max(o[0] for ho in opts for o in ho)
-    table = []
-    for ho in opts:
-        s = sorted(ho)
-        row, k, best_o = [None] * (maxc + 1), 0, None
-        for c in range(maxc + 1):
-            while k < len(s) and s[k][0] <= c:
-                if best_o is None or not (best_o[1] <= s[k][1]):
-                    best_o = s[k]
-                k += 1
-            row[c] = best_o
-        table.append(row)
+        _, h, c = pick
+        spare -= c - level[h]
+        level[h] = c
     rounds = 0
-    for _ in range(max_rounds):
-        changed = False
+    while rounds < max_rounds:
+        moved = False
         for i in range(H):
-            best_delta, bj, bi_o, bj_o = -1e-15, -1, None, None
-            slack = budget - used
-            for di in opts[i]:
-                if di[0] > cur[i][0] + slack:
+            for j in range(H):
+                if i == j:
                     continue
-                room = slack + cur[i][0] - di[0]
-                d_i = di[1] - cur[i][1]
-                if d_i < best_delta:
-                    best_delta, bj, bi_o, bj_o = d_i, i, di, di
-                for j in range(H):
-                    if j == i:
+                Fi, Fj = curves[i][0], curves[j][0]
+                best = None
+                for ci in range(level[i] + 1):
+                    if Fi[ci] == float("inf"):
                         continue
-                    uj = table[j][min(cur[j][0] + room, maxc)]
-                    if uj is None:
-                        continue
-                    d = d_i + (uj[1] - cur[j][1])
-                    if d < best_delta:
-                        best_delta, bj, bi_o, bj_o = d, j, di, uj
-            if bj >= 0:
-                used += bi_o[0] - cur[i][0]
-                cur[i] = bi_o
-                if bj != i:
-                    used += bj_o[0] - cur[bj][0]
-                    cur[bj] = bj_o
-                changed = True
-        if not changed:
+                    cj = min(maxc, level[j] + spare + (level[i] - ci))
+                    d = (Fi[ci] - Fi[level[i]]) + (Fj[cj] - Fj[level[j]])
+                    if d < -1e-12 * (Fi[level[i]] + Fj[level[j]]) and (best is None or d < best[0]):
+                        best = (d, ci, cj)
+                if best is not None:
+                    _, ci, cj = best
+                    spare += (level[i] - ci) - (cj - level[j])
+                    level[i], level[j] = ci, cj
+                    moved = True
+        if not moved:
             break
         rounds += 1
-    total = 0.0
-    for x in cur:
-        total += x[1]
-    return [(x[2], x[3]) for x in cur], rounds, total, True
+    alloc = [curves[h][1][level[h]] for h in range(H)]
+    total = sum(head_error(l, r, b, gamma) for l, (r, b) in zip(spectra, alloc))
+    return alloc, total, rounds

@@ -153,7 +153,7 @@ extern "C" kvq_status kvq_cobra_allocate(const double *spectra, int32_t n_heads,
     if (bits[i] < 1 || bits[i] > 16)
       return kvq::api_fail(KVQ_ERR_INVALID_ARG, "cobra allocate: bits must be in [1, 16]");
   const int H = n_heads;
-  std::vector<std::vector<CobraOpt>> opt(H), hull(H);
+  std::vector<std::vector<CobraOpt>> opt(H), hull(H), front(H);
   for (int h = 0; h < H; ++h) {
     const double *lam = spectra + (long long)h * 128;
     double pre[129];
@@ -178,6 +178,7 @@ extern "C" kvq_status kvq_cobra_allocate(const double *spectra, int32_t n_heads,
         if (!f.empty() && f.back().cost == x.cost) f.back() = x;
         else f.push_back(x);
       }
+    front[h] = f;
     for (const auto &x : f) {
       while (hull[h].size() >= 2) {
         const CobraOpt &a = hull[h][hull[h].size() - 2], &c = hull[h].back();
@@ -232,35 +233,153 @@ extern "C" kvq_status kvq_cobra_allocate(const double *spectra, int32_t n_heads,
     out = pref[h][lo - 1];
     return true;
   };
+  // Receivers' gains by extra bits: gtab[j][x] = the error head j sheds
+  // with x more bits (its best candidate within cur[j].cost + x); b1/b2: the
+  // two heads with the largest gain at each x.  A donor's move then finds
+  // its best receiver in one lookup.
+  long long maxc = 0;
+  for (int h = 0; h < H; ++h) maxc = std::max(maxc, by_cost[h].back().cost);
+  const size_t W = (size_t)maxc + 1;
+  std::vector<double> gtab((size_t)H * W);
+  std::vector<int> b1(W), b2(W);
+  auto fill_row = [&](int j) {
+    const auto &v = by_cost[j];
+    size_t k = 0;
+    double best = cur[j].err;
+    for (size_t x = 0; x < W; ++x) {
+      const long long lim = cur[j].cost + (long long)x;
+      while (k < v.size() && v[k].cost <= lim) best = std::min(best, v[k++].err);
+      gtab[(size_t)j * W + x] = cur[j].err - best;
+    }
+  };
+  auto fill_top = [&]() {
+    for (size_t x = 0; x < W; ++x) {
+      int f = -1, s2 = -1;
+      for (int j = 0; j < H; ++j) {
+        const double g = gtab[(size_t)j * W + x];
+        if (f < 0 || g > gtab[(size_t)f * W + x]) { s2 = f; f = j; }
+        else if (s2 < 0 || g > gtab[(size_t)s2 * W + x]) s2 = j;
+      }
+      b1[x] = f;
+      b2[x] = s2;
+    }
+  };
+  for (int j = 0; j < H; ++j) fill_row(j);
+  fill_top();
   int nround = 0;
   for (int it = 0; it < 64; ++it) {
     bool changed = false;
     for (int i = 0; i < H; ++i) {
       double best_delta = -1e-15;
       int bj = -1;
-      CobraOpt bi_opt{}, bj_opt{};
+      long long broom = 0;
+      CobraOpt bi_opt{};
       const long long slack = budget_bits - used;
       for (const auto &di : opt[i]) {
         if (di.cost > cur[i].cost + slack) continue;
-        const long long room = slack + cur[i].cost - di.cost;   // bits others may take
+        const long long room = std::min(slack + cur[i].cost - di.cost, maxc);   // bits others may take
         const double d_i = di.err - cur[i].err;
-        if (d_i < best_delta) { best_delta = d_i; bj = i; bi_opt = di; bj_opt = di; }
-        for (int j = 0; j < H; ++j) {
-          if (j == i) continue;
-          CobraOpt uj;
-          if (!best_within(j, cur[j].cost + room, uj)) continue;
-          const double d = d_i + (uj.err - cur[j].err);
-          if (d < best_delta) { best_delta = d; bj = j; bi_opt = di; bj_opt = uj; }
-        }
+        if (d_i < best_delta) { best_delta = d_i; bj = i; bi_opt = di; }
+        const int j = b1[room] != i ? b1[room] : b2[room];
+        if (j < 0) continue;
+        const double d = d_i - gtab[(size_t)j * W + room];
+        if (d < best_delta) { best_delta = d; bj = j; bi_opt = di; broom = room; }
       }
       if (bj >= 0) {
+        CobraOpt bj_opt = bi_opt;
+        if (bj != i && !best_within(bj, cur[bj].cost + broom, bj_opt)) continue;
         used += bi_opt.cost - cur[i].cost;
         cur[i] = bi_opt;
+        fill_row(i);
         if (bj != i) {
           used += bj_opt.cost - cur[bj].cost;
           cur[bj] = bj_opt;
+          fill_row(bj);
         }
+        fill_top();
         changed = true;
+      }
+    }
+    // Several donors for one receiver: a head moving up to a better
+    // candidate of its efficient frontier that does not fit is funded by
+    // downgrading other heads, the
+    // cheapest downgrade first (least error added per bit freed; a donor
+    // may step down more than once), when it gains more than they lose.
+    // Pairwise exchanges alone miss these.
+    {
+      struct Step {
+        double rate;
+        int h;
+        CobraOpt d;
+      };
+      auto worse = [](const Step &x, const Step &y) { return x.rate > y.rate; };   // min-heap
+      // each head's cheapest single downgrade from a candidate
+      auto step_from = [&](int i, const CobraOpt &from, Step &st) {
+        CobraOpt d;
+        if (from.cost == 0 || !best_within(i, from.cost - 1, d)) return false;
+        st = {(d.err - from.err) / (double)(from.cost - d.cost), i, d};
+        return true;
+      };
+      std::vector<Step> base;
+      auto rebuild = [&]() {
+        base.clear();
+        for (int i = 0; i < H; ++i) {
+          Step st;
+          if (step_from(i, cur[i], st)) base.push_back(st);
+        }
+      };
+      rebuild();
+      std::vector<CobraOpt> tent(H);
+      std::vector<char> touched(H);
+      std::vector<Step> heap;
+      for (int j = 0; j < H && !base.empty(); ++j) {
+        bool moved = false;
+        double mrate = -1.0;                     // cheapest downgrade per bit of the other heads
+        for (const auto &st : base)
+          if (st.h != j && (mrate < 0.0 || st.rate < mrate)) mrate = st.rate;
+        if (mrate < 0.0) continue;
+        for (const auto &upv : front[j]) {
+          if (upv.cost <= cur[j].cost || !(upv.err < cur[j].err)) continue;
+          long long need = upv.cost - cur[j].cost - (budget_bits - used);
+          if (need <= 0) continue;               // fits: the pairwise pass takes such moves
+          const double gain = cur[j].err - upv.err;
+          if (gain <= mrate * (double)need) continue;
+          double loss = 0.0;
+          heap.clear();
+          for (const auto &st : base)
+            if (st.h != j) heap.push_back(st);
+          std::make_heap(heap.begin(), heap.end(), worse);
+          for (int i = 0; i < H; ++i) { tent[i] = cur[i]; touched[i] = 0; }
+          while (need > 0 && loss < gain && !heap.empty()) {
+            std::pop_heap(heap.begin(), heap.end(), worse);
+            const Step st = heap.back();
+            heap.pop_back();
+            loss += st.d.err - tent[st.h].err;
+            need -= tent[st.h].cost - st.d.cost;
+            tent[st.h] = st.d;
+            touched[st.h] = 1;
+            Step nx;
+            if (step_from(st.h, tent[st.h], nx)) {
+              heap.push_back(nx);
+              std::push_heap(heap.begin(), heap.end(), worse);
+            }
+          }
+          if (need > 0 || !(loss < gain * (1.0 - 1e-12))) continue;
+          for (int i = 0; i < H; ++i)
+            if (touched[i]) {
+              used += tent[i].cost - cur[i].cost;
+              cur[i] = tent[i];
+            }
+          used += upv.cost - cur[j].cost;
+          cur[j] = upv;
+          changed = moved = true;
+          break;
+        }
+        if (moved) {
+          rebuild();
+          for (int h = 0; h < H; ++h) fill_row(h);
+          fill_top();
+        }
       }
     }
     if (!changed) break;

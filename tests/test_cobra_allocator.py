@@ -1,7 +1,9 @@
 """KV-COBRA per-head rank/bit allocation (host calibration step in libkvq)
-against the oracle's exact optimum (dynamic programming over the budget),
-the oracle against brute force, and the explainer's statements: the
-two-head worked example's split, C2 settling within five rounds, and the
+against the oracle: the exact optimum (dynamic programming over the
+budget, pinned by brute force), the continuous relaxation (weak duality)
+and the rounding gap a greedy fill can leave; the oracle's plain C1/C2
+reading of the explainer; and the explainer's statements: the two-head
+worked example's split, C2 settling within five rounds, and the
 calibration taking under 200 ms for a 256-head model (LLaMA-3.1-8B has
 8 kv heads x 32 layers)."""
 
@@ -76,43 +78,79 @@ def test_oracle_optimum_is_brute_force():
         assert (c1 is None and bf is None) or abs(c1[1] - bf[0]) < 1e-15
 
 
-def test_library_is_the_oracle_water_fill(L):
-    """The library runs the same C1/C2 steps as the oracle's plain
-    water_fill: identical allocation, rounds and total error, within the
-    budget.  Discrete water-filling with pairwise exchanges is not exact:
-    on 1-8 head problems with coarse candidates it stays within 20% of the
-    exact optimum (at 256 heads within 0.1%, next test)."""
-    rng = np.random.default_rng(11)
-    worst = 0.0
-    for _ in range(80):
-        H = int(rng.integers(1, 9))
-        sp = np.stack([_spectrum(rng, int(rng.integers(0, 3))) for _ in range(H)])
+def test_oracle_c1_and_plain_c2():
+    """C1 (each head's best error at every budget) against brute force over
+    the candidates; the plain C1/C2 reading of the explainer never beats
+    the exact optimum and respects the budget; the relaxation bound sits
+    below the optimum (weak duality)."""
+    rng = np.random.default_rng(4)
+    for _ in range(20):
+        H = int(rng.integers(1, 6))
+        sp = [_spectrum(rng, int(rng.integers(0, 3))) for _ in range(H)]
         budget = int(rng.integers(16 * H, 128 * 8 * H + 1))
-        alloc, rounds, lt = lib.cobra_allocate(sp, RANKS, BITS, budget)
-        oa, orounds, ot, fits = A.water_fill(list(sp), RANKS, BITS, budget)
-        assert fits and alloc == oa and rounds == orounds and lt == ot
-        assert sum(r * b for r, b in alloc) <= budget and rounds <= 5
-        tot, _ = A.optimum(list(sp), RANKS, BITS, budget)
-        assert tot - 1e-9 * max(1, tot) <= lt <= tot * 1.20 + 1e-12
-        worst = max(worst, lt / tot - 1)
-    print("worst gap to the exact optimum: %.3g" % worst)
+        errs, pick = A.c1_curve(sp[0], RANKS, BITS, 1024)
+        for c in range(0, 1025, 37):
+            bf = [A.head_error(sp[0], r, b) for r in RANKS for b in BITS if r * b <= c]
+            assert (not bf and pick[c] is None) or errs[c] == min(bf)
+        tot, _ = A.optimum(sp, RANKS, BITS, budget)
+        alloc, wt, _ = A.water_fill_plain(sp, RANKS, BITS, budget)
+        assert sum(r * b for r, b in alloc) <= budget and wt >= tot - 1e-12 * tot
+        lb, mu = A.lagrangian_bound(sp, RANKS, BITS, budget)
+        assert lb <= tot * (1 + 1e-12) + 1e-15 and mu >= 0.0
+        assert wt <= lb + A.rounding_gap(sp, RANKS, BITS, mu) + 1e-9 * tot
+
+
+def _check_against_optimum(sp, budget):
+    """The library's allocation against the oracle: within the budget, never
+    below the exact optimum, and within the relaxation's rounding gap of
+    the relaxation's optimum (what a greedy that fills heads by error
+    removed per bit is guaranteed to reach; exchange rounds only lower it)."""
+    alloc, rounds, lt = lib.cobra_allocate(np.stack(sp), RANKS, BITS, budget)
+    assert sum(r * b for r, b in alloc) <= budget
+    assert abs(lt - sum(A.head_error(l, r, b) for l, (r, b) in zip(sp, alloc))) <= 1e-12 * max(1.0, lt)
+    tot, _ = A.optimum(sp, RANKS, BITS, budget)
+    lb, mu = A.lagrangian_bound(sp, RANKS, BITS, budget)
+    assert lt >= tot - 1e-12 * max(1.0, tot)
+    assert lt <= lb + A.rounding_gap(sp, RANKS, BITS, mu) + 1e-9 * max(1.0, tot)
+    return (lt / tot - 1.0 if tot > 0 else 0.0), rounds, alloc
+
+
+def test_library_against_exact_optimum(L):
+    """1-8 heads, coarse candidates (8 ranks x 8 bit widths), budgets from
+    the cheapest to the richest: every case passes the relaxation bound and
+    settles within five exchange rounds; as a regression guard on these
+    seeded cases, at least 90% reach the exact optimum and none is more
+    than 12% above it (measured: 95% exact, worst 11.0%, 99th percentile
+    3%)."""
+    rng = np.random.default_rng(11)
+    gaps = []
+    for _ in range(280):
+        H = int(rng.integers(1, 9))
+        sp = [_spectrum(rng, int(rng.integers(0, 3))) for _ in range(H)]
+        budget = int(rng.integers(16 * H, 128 * 8 * H + 1))
+        gap, rounds, _ = _check_against_optimum(sp, budget)
+        assert rounds <= 5
+        gaps.append(gap)
+    gaps = np.array(gaps)
+    print("exact in %d of %d, worst gap %.4g" % ((gaps <= 1e-12).sum(), len(gaps), gaps.max()))
+    assert (gaps <= 1e-12).mean() >= 0.90 and gaps.max() <= 0.12
 
 
 @pytest.mark.parametrize("bpd", [0.5, 1, 2, 4])
 def test_256_heads_rounds_and_time(L, bpd):
+    """A 256-head model (8 kv heads x 32 layers): under 200 ms and at most
+    five C2 rounds (the explainer's figures), within 0.1% of the exact
+    optimum."""
     rng = np.random.default_rng(5)
     H = 256
-    sp = np.stack([_spectrum(rng, int(rng.integers(0, 3))) for _ in range(H)])
+    sp = [_spectrum(rng, int(rng.integers(0, 3))) for _ in range(H)]
     budget = int(bpd * 128 * H)
     t = time.perf_counter()
-    alloc, rounds, lt = lib.cobra_allocate(sp, RANKS, BITS, budget)
+    alloc, rounds, lt = lib.cobra_allocate(np.stack(sp), RANKS, BITS, budget)
     dt = time.perf_counter() - t
-    tot, _ = A.optimum(list(sp), RANKS, BITS, budget)
     assert rounds <= 5 and dt < 0.2, (rounds, dt)
-    assert sum(r * b for r, b in alloc) <= budget
-    assert lt <= tot * (1 + 1e-3) + 1e-12
-    oa, orounds, ot, _ = A.water_fill(list(sp), RANKS, BITS, budget)
-    assert alloc == oa and rounds == orounds and lt == ot
+    gap, _, _ = _check_against_optimum(sp, budget)
+    assert gap <= 1e-3
     # heads differ: the allocation spreads across ranks and bit widths
     assert len({r for r, _ in alloc}) > 1 and len({b for _, b in alloc}) > 1
 

@@ -115,3 +115,32 @@ def test_msb_first_packing_is_caught(monkeypatch):
         return np.packbits(flat, axis=-1, bitorder="big")
     monkeypatch.setattr(TO, "pack_codes", bad)
     _fails(TO.test_hand_worked_bit_patterns)
+
+
+def test_allocator_mutations_are_caught(monkeypatch):
+    """The KV-COBRA oracle: a C1 that ignores the budget boundary, and a
+    relaxation bound with the multiplier's sign flipped, each fail a pin."""
+    import oracle.allocator as OA
+    from tests import test_cobra_allocator as TCA
+
+    good = OA.head_error
+
+    def strict_c1(lam, ranks, bits, max_cost, gamma=OA.GAMMA):
+        errs, pick = [float("inf")] * (max_cost + 1), [None] * (max_cost + 1)
+        for c in range(max_cost + 1):
+            for r in ranks:
+                for b in bits:
+                    if r * b < c and good(lam, r, b, gamma) < errs[c]:      # '<' for '<='
+                        errs[c], pick[c] = good(lam, r, b, gamma), (r, b)
+        return errs, pick
+    monkeypatch.setattr(OA, "c1_curve", strict_c1)
+    _fails(TCA.test_oracle_c1_and_plain_c2)
+    monkeypatch.undo()
+
+    real = OA.lagrangian_bound
+
+    def flipped(spectra, ranks, bits, budget, gamma=OA.GAMMA):
+        v, mu = real(spectra, ranks, bits, budget, gamma)
+        return v + 2.0 * mu * budget, mu
+    monkeypatch.setattr(OA, "lagrangian_bound", flipped)
+    _fails(TCA.test_oracle_c1_and_plain_c2)
