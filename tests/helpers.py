@@ -163,3 +163,131 @@ def check_rotated_head(x, enc_gpu, spec, h, max_frac=1e-3):
 def unpack(cache, name, ospec, T):
     buf = download(cache, name)
     return OL.unpack_plane(buf, ospec, cache.batch, cache.n_kv_heads, cache.capacity, T), buf
+
+
+# ------------------------------------------------- precision of the kernels --
+
+def _softmax_stats(qh, K, V, sm_scale):
+    s = sm_scale * (K @ qh)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return p, p @ V
+
+
+def decode_bound(q, kenc, venc, ktail, vtail, kspec, vspec, T, N, sm_scale, tail_fmt="f16"):
+    """Elementwise bound on |device decode - oracle decode| [B, Hq, 128]
+    from the roundings the kernels make: a statistical model of the
+    rounding errors (each uniform over its half-width, std = half-width /
+    sqrt 3, independent), 8 standard deviations of their sum, plus
+    binary32 terms taken at their worst case.
+
+    Score errors (natural units), per token t:
+    * body keys on the integer matrix cores: the stored-basis query of each
+      head is rounded to a multiple of 2^-sh with 2^19 <= max|q'|*2^sh <
+      2^20, below max|q'|*2^-20 per component: std max|q'| 2^-20 |y_t| /
+      sqrt3 (y_t the stored-basis key); binary16 keys use hi + lo binary16
+      query parts (22 bits): 2^-22;
+    * tail keys: hi + lo binary16 parts (2^-22), bfloat16 parts (2^-16);
+    * binary32 query transforms (KVarN rotation, low-rank projection):
+      2^-22 of the transform's absolute sums per component;
+    * _1 keys: the block minimum times the block's query sum, in binary32.
+    A score error d_t moves the output by sum_t p_t (d_t - mean d)(v_t - o).
+    Value side: PV weights p * d_v as hi + lo binary16 (relative 2^-22) or
+    bfloat16 parts (2^-16); _1 values add sum_t p_t m_t in binary32; the
+    output transforms (inverse rotation, back projection) in binary32;
+    accumulation, exp2 and normalisation: 2^-20 of sum_t p_t |v_t| + |o|."""
+    q = np.asarray(q, np.float64)
+    B, Hq, _ = q.shape
+    Hkv = len(kenc[0])
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, 128))
+    for b in range(B):
+        for g in range(Hkv):
+            out[b, g * G:(g + 1) * G] = unit_bound(
+                q[b, g * G:(g + 1) * G], kenc[b][g], venc[b][g],
+                ktail[b, g] if N > 0 else None, vtail[b, g] if N > 0 else None,
+                kspec, vspec, g, T, N, sm_scale, tail_fmt)
+    return out
+
+
+def unit_bound(qg, kenc, venc, ktail, vtail, kspec, vspec, g, T, N, sm_scale, tail_fmt="f16"):
+    """decode_bound for one (batch entry, kv head g): qg [G, 128] its query
+    heads, kenc / venc its encodings, ktail / vtail its ring [N, 128]."""
+    import oracle.cobra as OC
+    import oracle.kvarn as OK
+    from oracle.codecs import decode_rows
+
+    r3 = np.sqrt(3.0)
+    tail_q = 2.0 ** (-16 if tail_fmt == "bf16" else -22)
+    tail_w = 2.0 ** (-16 if tail_fmt == "bf16" else -22)
+    u32 = 2.0 ** -22                     # binary32 sums, a few roundings each
+    G = qg.shape[0]
+    out = np.zeros((G, 128))
+    if True:
+        if True:
+            K = OL.dequant_head(kenc, kspec, g)[:T]
+            V = OL.dequant_head(venc, vspec, g)[:T]
+            tail = np.zeros(T, bool)
+            if N > 0:
+                for t in range(max(0, T - N), T):
+                    K[t] = ktail[t % N].astype(np.float64)
+                    V[t] = vtail[t % N].astype(np.float64)
+                    tail[t] = True
+            kc, vc = kspec.codec_of(g), vspec.codec_of(g)
+            Lk, Lv = kspec.block_len(g), vspec.block_len(g)
+            Yk = decode_rows(kenc, kc, Lk, rounded=False)[:T]
+            Yv = decode_rows(venc, vc, Lv, rounded=False)[:T]
+            kmin = kenc.get("mins") if kc != "f16" else None
+            vmin = venc.get("mins") if vc != "f16" else None
+            body_q = 2.0 ** (-20 if (kc != "f16" and vc != "f16") else -22)
+            for hh in range(G):
+                qh = np.asarray(qg[hh], np.float64)
+                if kspec.basis == "hadamard":
+                    wk = kspec.w[g].astype(np.float64)
+                    qs = OK.rotate(qh, 1.0 / wk) / 128.0
+                    qt = u32 * np.abs(qh / wk).sum() / 128.0 * np.ones_like(qs)
+                elif kspec.basis == "lowrank":
+                    Pk = kspec.P[g].astype(np.float64)
+                    qs = OC.project(qh, kspec.P[g])
+                    qt = u32 * (np.abs(Pk).T @ np.abs(qh))
+                else:
+                    qs, qt = qh, np.zeros_like(qh)
+                p, o = _softmax_stats(qh, K, V, sm_scale)
+                d_body = np.abs(qs).max() * body_q / r3 * np.linalg.norm(Yk, axis=1) + np.abs(Yk) @ qt
+                if kmin is not None:
+                    L = Lk
+                    qsum = np.abs(qs.reshape(-1, L).sum(1))
+                    d_body = d_body + u32 * (np.abs(kmin[:T]) @ qsum)
+                d = sm_scale * np.where(tail, np.abs(qh).max() * tail_q / r3 * np.linalg.norm(K, axis=1),
+                                        d_body)
+                ew = np.where(tail, tail_w, 2.0 ** -22) / r3
+                var = ((p * d)[:, None] ** 2 * (V - o) ** 2).sum(0) + ((p * ew)[:, None] ** 2 * V ** 2).sum(0)
+                floor = 2.0 ** -20 * ((p[:, None] * np.abs(V)).sum(0) + np.abs(o))
+                body = ~tail
+                if vmin is not None:
+                    mv = np.repeat(np.abs(vmin[:T]), Lv, axis=1)[:, : Yv.shape[1]]
+                    m_raw = (p[body, None] * mv[body]).sum(0)
+                else:
+                    m_raw = np.zeros(Yv.shape[1])
+                ob = (p[body, None] * np.abs(Yv[body])).sum(0) + m_raw     # stored-basis magnitudes
+                if vspec.basis == "hadamard":
+                    wv = vspec.w[g].astype(np.float64)
+                    floor = floor + u32 * ob.sum() / 128.0 / wv
+                elif vspec.basis == "lowrank":
+                    floor = floor + u32 * (np.abs(vspec.P[g].astype(np.float64)) @ ob)
+                else:
+                    floor = floor + u32 * m_raw
+                # transforms and merges mix channels: no channel's floor is
+                # below a 2^-2 share of the head's mean
+                floor = np.maximum(floor, 0.25 * floor.mean())
+                out[hh] = 8.0 * np.sqrt(var) + floor
+    return out
+
+
+def check_precision(got, ref, bound, what=""):
+    """|got - ref| <= bound elementwise; returns the worst ratio."""
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    ratio = float((err / bound).max())
+    print("precision %s: max err %.3g, max err/bound %.3g" % (what, float(err.max()), ratio))
+    assert ratio <= 1.0, (what, float(err.max()), ratio)
+    return ratio

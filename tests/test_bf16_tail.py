@@ -69,13 +69,17 @@ def test_decode_with_bf16_tail(gpu, name, T, N):
         rings[nm] = OL.tail_ring(x, N, fmt="bf16")
         H.upload(cache, nm, packed, OL.pack_tail(rings[nm], fmt="bf16"))
     cache.n_tokens = T
-    ref = OL.decode(q.numpy(), OL.encode_plane(k, ok_), OL.encode_plane(v, ov), rings["k"],
-                    rings["v"], ok_, ov, T, N, wl.sm_scale)
+    kenc, venc = OL.encode_plane(k, ok_), OL.encode_plane(v, ov)
+    ref = OL.decode(q.numpy(), kenc, venc, rings["k"], rings["v"], ok_, ov, T, N, wl.sm_scale)
+    bound = H.decode_bound(q.numpy(), kenc, venc, rings["k"], rings["v"], ok_, ov, T, N, wl.sm_scale,
+                           tail_fmt="bf16")
     for splits in (0, 3):
         out = cache.decode(q.to(gpu), wl.sm_scale, body_splits=splits)
         torch.cuda.synchronize()
-        err = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)))
+        got = out.cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(got - ref)))
         assert err <= H.ATOL, (name, T, N, splits, err)
+        H.check_precision(got, ref, bound, "%s T=%d N=%d bf16 splits=%d" % (name, T, N, splits))
     print("%s T=%d N=%d bf16 tail: max-abs %.2e" % (name, T, N, err))
 
 

@@ -31,6 +31,8 @@ def _run(gpu, wl, T, N, capacity, kc=None, vc=None, splits=(0,), seed_step=0, Hq
     cache.n_tokens = T
     ref = OL.decode(q.numpy(), kenc, venc, OL.tail_ring(k, N) if N else None,
                     OL.tail_ring(v, N) if N else None, ok_, ov, T, N, wl.sm_scale)
+    bound = H.decode_bound(q.numpy(), kenc, venc, OL.tail_ring(k, N) if N else None,
+                           OL.tail_ring(v, N) if N else None, ok_, ov, T, N, wl.sm_scale)
     outs = []
     for s in splits:
         out = cache.decode(q.to(gpu), wl.sm_scale, body_splits=s)
@@ -38,6 +40,7 @@ def _run(gpu, wl, T, N, capacity, kc=None, vc=None, splits=(0,), seed_step=0, Hq
         got = out.cpu().numpy().astype(np.float64)
         err = np.max(np.abs(got - ref))
         assert err <= H.ATOL, (wl.name, T, N, kc, vc, s, err)
+        H.check_precision(got, ref, bound, "%s T=%d N=%d %s/%s splits=%d" % (wl.name, T, N, kc, vc, s))
         outs.append(got)
     return outs
 

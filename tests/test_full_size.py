@@ -130,6 +130,9 @@ def _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated):
         err = float(np.max(np.abs(out[b, h * G:(h + 1) * G] - ref)))
         worst = max(worst, err)
         assert err <= H.ATOL, (wl.name, b, h, err)
+        bound = H.unit_bound(qh[b, h * G:(h + 1) * G], kenc, venc, kt, vt, ok_, ov, h, wl.T, wl.N,
+                             wl.sm_scale)
+        H.check_precision(out[b, h * G:(h + 1) * G], ref, bound, "%s unit (%d, %d)" % (wl.name, b, h))
     print("%s: %d units over T=%d, worst max-abs %.3g" % (wl.name, len(units), wl.T, worst))
 
 
@@ -150,14 +153,17 @@ def test_gqa4_32k_all_heads(gpu):
 def test_kvarn_q3_64k_sampled(gpu):
     wl = synth.WORKLOADS["kvarn_q3_tail2048"]
     cache, k, v, ok_, ov, out, qh = _build(gpu, wl)
-    _check_units(wl, cache, k, v, ok_, ov, out, qh, [(0, 0), (1, 5), (3, 7)], rotated=True)
+    units = [(0, h) for h in range(wl.Hkv)] + [(1, 5), (3, 7)]
+    _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated=True)
 
 
 def test_lowrank_128k_sampled(gpu):
     wl = synth.WORKLOADS["lowrank_1bpd"]
     cache, k, v, ok_, ov, out, qh = _build(gpu, wl)
-    # ranks 128, 16 and 32 (head 0, 3, 6 of the table)
-    _check_units(wl, cache, k, v, ok_, ov, out, qh, [(0, 0), (5, 3), (7, 6)], rotated=True)
+    # every kv head (every rank and bit width of the table) of batch entry 0,
+    # and heads 3 and 6 of later entries
+    units = [(0, h) for h in range(wl.Hkv)] + [(5, 3), (7, 6)]
+    _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated=True)
 
 
 def test_vbr_128k_layers_and_transcode(gpu):
@@ -182,6 +188,9 @@ def test_vbr_128k_layers_and_transcode(gpu):
             ref = _unit_outputs(wl_l, kenc, venc, None, None, ok_, ov, h, qh[0])
             err = float(np.max(np.abs(out[0, h * G:(h + 1) * G] - ref)))
             assert err <= H.ATOL, (codec, h, err)
+            bound = H.unit_bound(qh[0, h * G:(h + 1) * G], kenc, venc, None, None, ok_, ov, h, wl.T, 0,
+                                 wl.sm_scale)
+            H.check_precision(out[0, h * G:(h + 1) * G], ref, bound, "vbr %s head %d" % (codec, h))
         if codec == "f16":
             dst = cache.transcode("q8_0", "q8_0")
             torch.cuda.synchronize()

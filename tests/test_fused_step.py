@@ -107,13 +107,18 @@ def test_step_matches_two_calls_and_oracle(gpu, name, kc, vc, Hq, T0, N, fmt, ra
             ring = np.concatenate([OL.tail_ring(x[b:b + 1, :T1[b]], N, fmt=fmt) for b in range(B)])
             assert np.array_equal(dev["tail"], OL.pack_tail(ring, fmt=fmt)), name_
     ref = np.zeros(outs[0].shape)
+    bound = np.zeros(outs[0].shape)
     for b in range(B):
         kb, vb = k[b:b + 1, :T1[b]], v[b:b + 1, :T1[b]]
-        ref[b] = OL.decode(q.numpy()[b:b + 1], OL.encode_plane(kb, ok_), OL.encode_plane(vb, ov),
-                           OL.tail_ring(kb, N, fmt=fmt) if N else None,
-                           OL.tail_ring(vb, N, fmt=fmt) if N else None, ok_, ov, T1[b], N, wl.sm_scale)[0]
+        ke, ve = OL.encode_plane(kb, ok_), OL.encode_plane(vb, ov)
+        kt = OL.tail_ring(kb, N, fmt=fmt) if N else None
+        vt = OL.tail_ring(vb, N, fmt=fmt) if N else None
+        ref[b] = OL.decode(q.numpy()[b:b + 1], ke, ve, kt, vt, ok_, ov, T1[b], N, wl.sm_scale)[0]
+        bound[b] = H.decode_bound(q.numpy()[b:b + 1], ke, ve, kt, vt, ok_, ov, T1[b], N, wl.sm_scale,
+                                  tail_fmt=fmt)[0]
     err = float(np.max(np.abs(outs[0].astype(np.float64) - ref)))
     assert err <= H.ATOL, err
+    H.check_precision(outs[0], ref, bound, "%s %s/%s Hq=%d N=%d %s" % (name, kc, vc, Hq, N, fmt))
 
 
 def test_lowrank_step_two_launches(gpu):
