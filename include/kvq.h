@@ -202,6 +202,22 @@ kvq_status kvq_append_decode(const kvq_layer *layer, const float *k_new, const f
                              const float *q, int32_t n_q_heads, float sm_scale, float *out,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* kvq_append_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The decode workspace is a
+ * fixed 16 MiB device array inside the library (one per GPU, held until the
+ * process ends); the call allocates and frees nothing.  The first call on a
+ * GPU also enqueues a small kernel that clears the array's completion
+ * counters; every completed call leaves them clear.  All calls on one GPU
+ * share the array: calls that overlap in time on one GPU (on any streams)
+ * race and must not be issued.  KVQ_ERR_WORKSPACE (nothing enqueued) when
+ * the layer's step needs more than 16 MiB of workspace (the workspace
+ * kvq_decode_workspace_bytes reports for the plan chosen; grows with
+ * batch x query heads); other arguments and errors as kvq_append_decode. */
+kvq_status kvq_append_decode_noalloc(const kvq_layer *layer, const float *k_new, const float *v_new,
+                                     const float *q, int32_t n_q_heads, float sm_scale, float *out,
+                                     void *stream);
+
 /* Workspace needed by kvq_decode_attention for this layer's shapes and
  * capacity (independent of n_tokens), in bytes.  Its first 64 KiB hold
  * split-completion counters: zero-fill a workspace once before its first

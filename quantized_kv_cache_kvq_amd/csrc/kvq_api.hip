@@ -378,9 +378,10 @@ namespace {
 // Decode of `layer` (already validated).  Fused step: k_new / v_new non-null
 // and layer.n_tokens already counting the new token (the kernel writes it);
 // seq_add is added to every seq_tokens entry.
+// check_only: run every check, launch nothing.
 kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, float sm_scale,
                        float *out, void *ws, size_t ws_bytes, int32_t body_splits, void *stream,
-                       const float *k_new, const float *v_new, int seq_add) {
+                       const float *k_new, const float *v_new, int seq_add, bool check_only = false) {
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q / out is NULL");
   if (n_q_heads < 1 || n_q_heads % L.n_kv_heads)
     return fail(KVQ_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
@@ -534,6 +535,7 @@ kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, fl
     return fail(KVQ_ERR_UNSUPPORTED, "batch x kv heads x head groups = %d above %d", units,
                 DECODE_MAX_UNITS);
 
+  if (check_only) return KVQ_OK;
   uint8_t *wsb = reinterpret_cast<uint8_t *>(ws);
   DecodeArgs a;
   memset(&a, 0, sizeof a);
@@ -589,9 +591,15 @@ kvq_status kvq_decode_attention_splits(const kvq_layer *layer, const float *q, i
                      nullptr, nullptr, 0);
 }
 
-kvq_status kvq_append_decode(const kvq_layer *layer, const float *k_new, const float *v_new,
-                             const float *q, int32_t n_q_heads, float sm_scale, float *out,
-                             void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode step (append + decode) on a given workspace; check_only runs
+// every check and launches nothing.
+kvq_status append_decode_impl(const kvq_layer *layer, const float *k_new, const float *v_new,
+                              const float *q, int32_t n_q_heads, float sm_scale, float *out, void *ws,
+                              size_t ws_bytes, void *stream, bool check_only) {
   kvq_status s = check_layer(layer);
   if (s != KVQ_OK) return s;
   if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "k_new / v_new is NULL");
@@ -603,14 +611,97 @@ kvq_status kvq_append_decode(const kvq_layer *layer, const float *k_new, const f
   const int G = n_q_heads > 0 && n_q_heads % layer->n_kv_heads == 0 ? n_q_heads / layer->n_kv_heads : 0;
   const bool fused = G > 0 && decode_head_group(G) == G && layer->k.basis != KVQ_BASIS_LOWRANK;
   if (fused)
-    return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, k_new, v_new, 1);
+    return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, k_new, v_new, 1,
+                       check_only);
   // not fusable here (several head groups per kv head read the same tiles,
-  // or low rank): the append launch, then the decode launch
+  // or low rank): the append launch, then the decode launch -- after the
+  // decode's own checks, so that an error enqueues nothing
+  s = decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, nullptr, nullptr, 1, true);
+  if (s != KVQ_OK || check_only) return s;
   const PlaneArgs kp = plane_args(*layer, layer->k), vp = plane_args(*layer, layer->v);
   hipError_t e = launch_append(kp, vp, k_new, v_new, layer->batch, 1, layer->n_tokens,
                                layer->seq_tokens, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, nullptr, nullptr, 1);
+}
+
+// Scratch of the allocation-free step: the decode workspace (completion
+// counters, prepared query, split partials) in a fixed device array.  Each
+// GPU the library runs on holds its own copy for the life of the process;
+// host code reaches it only through the address hipGetSymbolAddress gives
+// on that device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+struct ScratchDev {
+  void *ptr = nullptr;   // device address of `scratch` on this device
+  bool armed = false;    // completion counters cleared
+};
+constexpr int SCRATCH_MAX_DEVICES = 64;
+ScratchDev g_scratch[SCRATCH_MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_append_decode(const kvq_layer *layer, const float *k_new, const float *v_new,
+                             const float *q, int32_t n_q_heads, float sm_scale, float *out,
+                             void *ws, size_t ws_bytes, void *stream) {
+  return append_decode_impl(layer, k_new, v_new, q, n_q_heads, sm_scale, out, ws, ws_bytes, stream,
+                            false);
+}
+
+kvq_status kvq_append_decode_noalloc(const kvq_layer *layer, const float *k_new, const float *v_new,
+                                     const float *q, int32_t n_q_heads, float sm_scale, float *out,
+                                     void *stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(KVQ_ERR_UNSUPPORTED, "device %d above the %d the allocation-free step tracks", dev,
+                SCRATCH_MAX_DEVICES);
+  void *ptr = nullptr;
+  bool armed = false;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev].ptr) {
+      void *p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      g_scratch[dev].ptr = p;
+    }
+    ptr = g_scratch[dev].ptr;
+    armed = g_scratch[dev].armed;
+  }
+  kvq_status s = append_decode_impl(layer, k_new, v_new, q, n_q_heads, sm_scale, out, ptr,
+                                    NOALLOC_SCRATCH_BYTES, stream, true);
+  if (s == KVQ_ERR_WORKSPACE) {
+    char detail[512];
+    snprintf(detail, sizeof detail, "%s", g_err);
+    return fail(KVQ_ERR_WORKSPACE, "kvq_append_decode_noalloc: the layer needs more scratch than the "
+                "fixed %zu bytes (%s); use kvq_append_decode with a workspace", NOALLOC_SCRATCH_BYTES,
+                detail);
+  }
+  if (s != KVQ_OK) return s;
+  if (!armed) {
+    // the completion counters start at zero; every completed step leaves
+    // them zero again
+    const int n = (int)(DECODE_CNT_BYTES / sizeof(uint32_t));
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<uint32_t *>(ptr), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch counter clear");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch[dev].armed = true;
+  }
+  return append_decode_impl(layer, k_new, v_new, q, n_q_heads, sm_scale, out, ptr, NOALLOC_SCRATCH_BYTES,
+                            stream, false);
 }
 
 kvq_status kvq_decode_attention(const kvq_layer *layer, const float *q, int32_t n_q_heads,

@@ -82,6 +82,9 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]),
+    "kvq_append_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                                 ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
     "kvq_decode_attention": (ctypes.c_int, [ctypes.POINTER(kvq_layer), ctypes.c_void_p, ctypes.c_int32,
                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
@@ -173,6 +176,12 @@ def decode_workspace_bytes(layer, n_q_heads):
 def append_decode(layer, k_ptr, v_ptr, q_ptr, n_q_heads, sm_scale, out_ptr, ws_ptr, ws_bytes, stream):
     check(load().kvq_append_decode(ctypes.byref(layer), k_ptr, v_ptr, q_ptr, n_q_heads,
                                    ctypes.c_float(sm_scale), out_ptr, ws_ptr, ws_bytes, stream))
+
+
+def append_decode_noalloc(layer, k_ptr, v_ptr, q_ptr, n_q_heads, sm_scale, out_ptr, stream):
+    """The one-call step with the library's fixed scratch as its workspace."""
+    check(load().kvq_append_decode_noalloc(ctypes.byref(layer), k_ptr, v_ptr, q_ptr, n_q_heads,
+                                           ctypes.c_float(sm_scale), out_ptr, stream))
 
 
 def decode_attention(layer, q_ptr, n_q_heads, sm_scale, out_ptr, ws_ptr, ws_bytes, stream,
