@@ -1,19 +1,20 @@
-// Append kernel: rotate / project, block-quantise, bit-pack and store new
-// tokens, plus their 16-bit precision-tail copy.
-//
-// One wave (64 lanes) per item = (batch entry, new token, kv head, K|V);
-// 8-wave workgroups stride over the items.  Lane l owns raw channels 2l,
-// 2l+1.  Steps, after the BeeLlama v0.4.0 notes (KVarN and precision-tail
-// sections) and the KV-COBRA explainer (projection with the Hadamard
-// rotation fused in):
+// Append kernels: rotate / project, block-quantise, bit-pack and store new
+// tokens, plus their 16-bit precision-tail copy.  Steps, after the BeeLlama
+// v0.4.0 notes (KVarN and precision-tail sections) and the KV-COBRA
+// explainer (projection with the Hadamard rotation fused in):
 //   1. tail copy: the raw vector rounded to the tail format (binary16 or
 //      bfloat16) into ring slot t mod tail_len;
-//   2. stored coordinates: x (plain), H (x * w) by an in-wave fast
-//      Walsh-Hadamard transform (hadamard), or P_h^T x (low rank);
+//   2. stored coordinates: x (plain), H (x * w) by a fast Walsh-Hadamard
+//      transform (hadamard), or P_h^T x (low rank);
 //   3. per 32-block (or min(32, rank) block) scale (and min);
 //   4. codes with correctly rounded binary32 division and rint (ties even):
 //      this reproduces the exact-quotient definition bit for bit;
 //   5. bit-pack the row and store it in the 64-token tiled layout.
+// Three kernels: layers with only plain / KVarN planes take one lane per
+// (token, 32-channel block) (append_flat_kernel); layers with a low-rank
+// plane take one wave per (token, kv head, K|V) item (append_kernel), and
+// prefill-sized low-rank appends project on the matrix cores
+// (append_lowrank_kernel).
 #include "kvq_common.hpp"
 #include "kvq_internal.hpp"
 
@@ -273,6 +274,226 @@ __global__ __launch_bounds__(64 * AP_WAVES) void append_kernel(PlaneArgs kp, Pla
 }
 
 
+// The scalar fields of one plain or KVarN plane that append_flat_kernel
+// reads, picked from the K or V argument with scalar selects (a run-time
+// choice between the two argument blocks would copy them to scratch).
+struct RowPlane {
+  uint8_t *codes;
+  uint16_t *scales;
+  uint16_t *mins;
+  uint16_t *tail;
+  const float *w;
+  int codec, basis, hkv, capacity, tail_len, tail_bf16;
+};
+
+__device__ __forceinline__ RowPlane row_plane(const PlaneArgs &kp, const PlaneArgs &vp, bool v) {
+  RowPlane r;
+  r.codes = v ? vp.codes : kp.codes;
+  r.scales = v ? vp.scales : kp.scales;
+  r.mins = v ? vp.mins : kp.mins;
+  r.tail = v ? vp.tail : kp.tail;
+  r.w = v ? vp.w : kp.w;
+  r.codec = v ? vp.codec : kp.codec;
+  r.basis = v ? vp.basis : kp.basis;
+  r.hkv = v ? vp.hkv : kp.hkv;
+  r.capacity = v ? vp.capacity : kp.capacity;
+  r.tail_len = v ? vp.tail_len : kp.tail_len;
+  r.tail_bf16 = v ? vp.tail_bf16 : kp.tail_bf16;
+  return r;
+}
+
+// Layers whose K and V planes are both plain or KVarN, one lane per
+// (new token, 32-channel block): a wave takes 16 consecutive new tokens of
+// one plane x 4 blocks (lane 4r + j = token r, block j), a 256-thread
+// workgroup 64 tokens.  Each lane reads its block's 32 binary32 values
+// (128 contiguous bytes), and quantises it on its own (maximum, scale,
+// codes, packing in registers), so no row-wide reduction crosses lanes; the
+// 16 tokens' chunks of one block are contiguous in the 64-token tiled
+// layout, so the code, scale and tail stores of a wave fill whole lines.
+// The KVarN transform (sign vector, then the Walsh-Hadamard butterflies in
+// increasing stride) runs strides 1..16 inside the lane and strides 32, 64
+// between the four lanes of a token (quad DPP), with the same butterflies
+// and order as the one-row-per-wave transform, so both give the same bits.
+constexpr int AF_TOKENS = 64;                    // tokens per workgroup
+constexpr int AF_THREADS = 4 * AF_TOKENS;
+
+// Partner lane's value in the same quad: xor 1 (QP = 0xB1) or xor 2 (0x4E).
+template <int QP>
+__device__ __forceinline__ float quad_xor(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), QP, 0xF, 0xF, true));
+}
+
+// Block j (32 values x) of token t of the plane whose rows start at row
+// `rows`: scale (and min), codes, packed field, stored in the tiled layout.
+template <int CODEC>
+__device__ __forceinline__ void encode_block_lane(const RowPlane &p, long long rows, int t, int j,
+                                                  const float (&x)[32]) {
+  constexpr int RB = row_bytes(CODEC, D);
+  uint8_t *tile = p.codes + rows * RB + (long long)(t >> 6) * (TILE * RB);
+  const int tt = t & (TILE - 1);
+  auto chunk_ptr = [&](int byte) { return tile + ((byte >> 4) * TILE + tt) * 16 + (byte & 15); };
+  if constexpr (CODEC == KVQ_F16) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = (uint32_t)f32_to_f16_bits(x[8 * s + 2 * e]) | ((uint32_t)f32_to_f16_bits(x[8 * s + 2 * e + 1]) << 16);
+      *reinterpret_cast<u32x4 *>(chunk_ptr(64 * j + 16 * s)) = v;
+    }
+  } else {
+    constexpr int BITS = codec_bits(CODEC), FAM = codec_family(CODEC);
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    const long long so = (rows + t) * (D / 32) + j;
+    float d, m = 0.f;
+    uint32_t q[32];
+    if constexpr (FAM == FAM_0) {
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+      const uint16_t dh = f32_to_f16_bits(amax / qmax);
+      p.scales[so] = dh;
+      d = f16_bits_to_f32(dh);
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        q[e] = d != 0.f ? (uint32_t)(int)fminf(fmaxf(rintf(x[e] / d), -qmax), qmax) & mask : 0u;
+    } else {
+      float lo = x[0], hi = x[0];
+#pragma unroll
+      for (int e = 1; e < 32; ++e) {
+        lo = fminf(lo, x[e]);
+        hi = fmaxf(hi, x[e]);
+      }
+      const uint16_t mh = f32_to_f16_bits(lo);
+      m = f16_bits_to_f32(mh);
+      constexpr float levels = (float)((1 << BITS) - 1);
+      const uint16_t dh = f32_to_f16_bits((hi - m) / levels);
+      p.scales[so] = dh;
+      p.mins[so] = mh;
+      d = f16_bits_to_f32(dh);
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        q[e] = d != 0.f ? (uint32_t)(int)fminf(fmaxf(rintf((x[e] - m) / d), 0.f), levels) : 0u;
+    }
+    // the block's field: code e at bits [e BITS, (e + 1) BITS), BITS dwords
+    uint32_t w[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k] = 0u;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int bit = e * BITS;
+      w[bit >> 5] |= q[e] << (bit & 31);
+      if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= q[e] >> (32 - (bit & 31));
+    }
+    if constexpr (BITS % 4 == 0) {
+#pragma unroll
+      for (int s = 0; s < BITS / 4; ++s)
+        *reinterpret_cast<u32x4 *>(chunk_ptr(4 * BITS * j + 16 * s)) = u32x4{w[4 * s], w[4 * s + 1], w[4 * s + 2], w[4 * s + 3]};
+    } else {
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) *reinterpret_cast<uint32_t *>(chunk_ptr(4 * BITS * j + 4 * k)) = w[k];
+    }
+  }
+}
+
+__global__ __launch_bounds__(AF_THREADS) void append_flat_kernel(PlaneArgs kp, PlaneArgs vp,
+                                                                 const float *__restrict__ k_new,
+                                                                 const float *__restrict__ v_new, int n_new,
+                                                                 int t0, int batch,
+                                                                 const int32_t *__restrict__ seq) {
+  __shared__ float wsh[D];
+  const bool isv = (int)blockIdx.z >= batch;
+  const int b = isv ? (int)blockIdx.z - batch : (int)blockIdx.z;
+  const int h = blockIdx.y;
+  const RowPlane p = row_plane(kp, vp, isv);
+  const bool rot = p.basis == KVQ_BASIS_HADAMARD;
+  if (rot) {
+    if (threadIdx.x < D / 4)
+      reinterpret_cast<float4 *>(wsh)[threadIdx.x] = reinterpret_cast<const float4 *>(p.w + (long long)h * D)[threadIdx.x];
+    __syncthreads();
+  }
+  const int i = (int)blockIdx.x * AF_TOKENS + (int)(threadIdx.x >> 2);
+  const int j = threadIdx.x & 3;
+  if (i >= n_new) return;                          // all four lanes of a token leave together
+  const int t = (seq ? seq[b] : t0) + i;
+  if ((unsigned)t >= (unsigned)p.capacity) return;   // ragged position out of contract: no write
+  const float *src = (isv ? v_new : k_new) + (((long long)b * n_new + i) * p.hkv + h) * D + 32 * j;
+  float x[32];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const float4 v = reinterpret_cast<const float4 *>(src)[s];
+    x[4 * s] = v.x;
+    x[4 * s + 1] = v.y;
+    x[4 * s + 2] = v.z;
+    x[4 * s + 3] = v.w;
+  }
+  const long long plane = (long long)b * p.hkv + h;
+  // precision tail: the raw values of the newest tail_len tokens of this call
+  if (p.tail_len > 0 && i + p.tail_len >= n_new) {
+    const int slot = t % p.tail_len;
+    uint8_t *tile = reinterpret_cast<uint8_t *>(p.tail) + plane * p.tail_len * (2 * D) +
+                    (long long)(slot >> 6) * (TILE * 2 * D);
+    const int st = slot & (TILE - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = x[8 * s + 2 * e], hi = x[8 * s + 2 * e + 1];
+        v[e] = p.tail_bf16 ? (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16)
+                           : (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+      }
+      *reinterpret_cast<u32x4 *>(tile + ((4 * j + s) * TILE + st) * 16) = v;
+    }
+  }
+  if (rot) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float4 wv = reinterpret_cast<const float4 *>(wsh + 32 * j)[s];
+      x[4 * s] *= wv.x;
+      x[4 * s + 1] *= wv.y;
+      x[4 * s + 2] *= wv.z;
+      x[4 * s + 3] *= wv.w;
+    }
+    // strides 1 .. 16 inside the lane: (u, v) -> (u + v, u - v)
+#pragma unroll
+    for (int st = 1; st < 32; st <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        if (e & st) continue;
+        const float u = x[e], v = x[e + st];
+        x[e] = u + v;
+        x[e + st] = u - v;
+      }
+    }
+    // strides 32 and 64: partner lane j ^ 1, j ^ 2 of the same token
+    const bool up1 = (j & 1) != 0, up2 = (j & 2) != 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float px = quad_xor<0xB1>(x[e]);
+      x[e] = up1 ? px - x[e] : x[e] + px;
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float px = quad_xor<0x4E>(x[e]);
+      x[e] = up2 ? px - x[e] : x[e] + px;
+    }
+  }
+  const long long rows = plane * p.capacity;
+  switch (p.codec) {
+#define KVQ_FLAT_CASE(CC) \
+  case CC: encode_block_lane<CC>(p, rows, t, j, x); break;
+    KVQ_FLAT_CASE(KVQ_F16)
+    KVQ_FLAT_CASE(KVQ_Q8_0) KVQ_FLAT_CASE(KVQ_Q6_0) KVQ_FLAT_CASE(KVQ_Q5_0) KVQ_FLAT_CASE(KVQ_Q4_0)
+    KVQ_FLAT_CASE(KVQ_Q3_0) KVQ_FLAT_CASE(KVQ_Q2_0)
+    KVQ_FLAT_CASE(KVQ_Q8_1) KVQ_FLAT_CASE(KVQ_Q6_1) KVQ_FLAT_CASE(KVQ_Q5_1) KVQ_FLAT_CASE(KVQ_Q4_1)
+    KVQ_FLAT_CASE(KVQ_Q3_1) KVQ_FLAT_CASE(KVQ_Q2_1) KVQ_FLAT_CASE(KVQ_Q1_1)
+#undef KVQ_FLAT_CASE
+    default: break;
+  }
+}
+
 // Low-rank planes, prefill-sized appends: u = P_h^T x for 16 tokens at a
 // time on the matrix cores (v_mfma_f32_16x16x32_f16), so P_h is read once
 // per 64 tokens instead of once per token.  A workgroup of 4 waves takes 64
@@ -406,9 +627,11 @@ hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *
   } else if (kp.basis == KVQ_BASIS_LOWRANK || vp.basis == KVQ_BASIS_LOWRANK)
     hipLaunchKernelGGL(append_kernel<true>, dim3((unsigned)blocks), dim3(64 * AP_WAVES), 0, stream, kp,
                        vp, k_new, v_new, n_new, t0, batch, seq, (unsigned)items);
-  else
-    hipLaunchKernelGGL(append_kernel<false>, dim3((unsigned)blocks), dim3(64 * AP_WAVES), 0, stream, kp,
-                       vp, k_new, v_new, n_new, t0, batch, seq, (unsigned)items);
+  else {
+    const dim3 grid((unsigned)((n_new + AF_TOKENS - 1) / AF_TOKENS), (unsigned)kp.hkv, (unsigned)(2 * batch));
+    hipLaunchKernelGGL(append_flat_kernel, grid, dim3(AF_THREADS), 0, stream, kp, vp, k_new, v_new, n_new, t0,
+                       batch, seq);
+  }
   return hipGetLastError();
 }
 

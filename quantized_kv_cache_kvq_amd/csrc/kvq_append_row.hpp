@@ -49,36 +49,53 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Per-block scale (and min), codes and bit-packed row of one token whose
-// stored coordinates are held two per lane (a = coordinate 2l, c = 2l + 1),
-// for a plain or KVarN plane of a fixed codec: blocks of 32 are the 16
-// lanes of a DPP row, so every reduction is a row reduction and nothing goes
-// through LDS except the 3/5/6-bit pack.  `rows` = rows before this
-// (b, kv head) plane.
+// Unsigned all-reduce steps over lanes of a DPP row; with full row and bank
+// masks the move folds into the consuming ALU instruction.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t row_umax16(uint32_t x) {
+  x = max(x, dpp_u<0x128>(x));
+  x = max(x, dpp_u<0x124>(x));
+  x = max(x, dpp_u<0x122>(x));
+  return max(x, dpp_u<0x121>(x));
+}
+// OR over each aligned group of K lanes (K = 2, 4, 8, 16), every lane of the
+// group receiving it: quad swaps (1 0 3 2, then 2 3 0 1), then the half-row
+// and row mirrors, which pair each quad / half with the other.
+template <int K>
+__device__ __forceinline__ uint32_t group_or(uint32_t w) {
+  w |= dpp_u<0xB1>(w);
+  if constexpr (K >= 4) w |= dpp_u<0x4E>(w);
+  if constexpr (K >= 8) w |= dpp_u<0x141>(w);
+  if constexpr (K >= 16) w |= dpp_u<0x140>(w);
+  return w;
+}
+
+// Per-block scale (and min) and codes of one token whose stored coordinates
+// are held two per lane (a = coordinate 2l, c = 2l + 1), for a plain or
+// KVarN plane of a fixed codec: blocks of 32 are the 16 lanes of a DPP row,
+// so every reduction is a row reduction.  Returns this lane's 2*BITS code
+// bits (codes of coordinates 2l, 2l + 1 at bits [0, BITS), [BITS, 2 BITS));
+// dh / mh: the binary16 bits of the lane's block scale (and min).  Inputs
+// are finite: the block maximum of |x| is taken on the bit patterns.
 template <int BITS, int FAM>
-__device__ __forceinline__ void quantize_row(const PlaneArgs &p, long long rows, int t, float a, float c,
-                                             uint32_t *stage) {
-  constexpr int RB = row_bytes(FAM == FAM_0 ? KVQ_Q8_0 : KVQ_Q8_1, D) * BITS / 8;   // 16 * BITS
-  constexpr int CK = chunk_bytes(RB);
-  const int lane = threadIdx.x & 63;
-  const long long so = (rows + t) * 4 + (lane >> 4);
+__device__ __forceinline__ uint32_t row_fields(float a, float c, uint16_t &dh, uint16_t &mh) {
   float d, m = 0.f;
   if constexpr (FAM == FAM_0) {
-    const float amax = row_max16(fmaxf(fabsf(a), fabsf(c)));
+    const uint32_t ua = __float_as_uint(a) & 0x7fffffffu, uc = __float_as_uint(c) & 0x7fffffffu;
+    const float amax = __uint_as_float(row_umax16(max(ua, uc)));
     constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
-    const uint16_t dh = f32_to_f16_bits(amax / qmax);
-    if ((lane & 15) == 0) p.scales[so] = dh;
+    dh = f32_to_f16_bits(amax / qmax);
+    mh = 0;
     d = f16_bits_to_f32(dh);
   } else {
     const float lo = row_min16(fminf(a, c)), hi = row_max16(fmaxf(a, c));
-    const uint16_t mh = f32_to_f16_bits(lo);
+    mh = f32_to_f16_bits(lo);
     m = f16_bits_to_f32(mh);
     constexpr float levels = (float)((1 << BITS) - 1);
-    const uint16_t dh = f32_to_f16_bits((hi - m) / levels);
-    if ((lane & 15) == 0) {
-      p.scales[so] = dh;
-      p.mins[so] = mh;
-    }
+    dh = f32_to_f16_bits((hi - m) / levels);
     d = f16_bits_to_f32(dh);
   }
   constexpr uint32_t mask = (1u << BITS) - 1u;
@@ -94,56 +111,96 @@ __device__ __forceinline__ void quantize_row(const PlaneArgs &p, long long rows,
       q1 = (uint32_t)(int)fminf(fmaxf(rintf((c - m) / d), 0.f), levels);
     }
   }
-  // this lane's 2*BITS bits start at bit 2*BITS*lane of the row
-  const uint32_t v = (q0 & mask) | ((q1 & mask) << BITS);
-  uint8_t *tile = p.codes + rows * RB + (long long)(t / TILE) * TILE * RB;
-  const int tt = t % TILE;
+  return (q0 & mask) | ((q1 & mask) << BITS);
+}
+
+// The packed row (16 * BITS bytes, this lane's bits at bit 2*BITS*lane) into
+// LDS at `row` (dword aligned): 8/4/2/1-bit fields are OR-ed across lanes
+// by DPP and written a dword per group of lanes; 3/5/6-bit fields are OR-ed
+// into the zeroed row by LDS atomics.  Ends with the row complete in LDS.
+template <int BITS>
+__device__ __forceinline__ void pack_row_lds(uint32_t v, uint32_t *row) {
+  const int lane = threadIdx.x & 63;
   if constexpr (BITS == 8 || BITS == 4 || BITS == 2 || BITS == 1) {
     constexpr int K = 16 / BITS;                   // lanes per dword
-    uint32_t w = v << (2 * BITS * (lane % K));
-#pragma unroll
-    for (int o = 1; o < K; o <<= 1) w |= __shfl_xor(w, o, 64);
-    if (lane % K == 0) {
-      const int byte = 4 * (lane / K);
-      *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = w;
-    }
+    const uint32_t w = group_or<K>(v << (2 * BITS * (lane % K)));
+    if (lane % K == 0) row[lane / K] = w;
   } else {
-    // 3, 5, 6 bits: OR each lane's field into the row's dwords in LDS
-    if (lane < RB / 4) stage[lane] = 0u;
+    constexpr int NW = 4 * BITS;                   // dwords of the row
+    if (lane < NW) row[lane] = 0u;
     wave_sync();
     const int o = 2 * BITS * lane, k = o >> 5, sh = o & 31;
-    __hip_atomic_fetch_or(stage + k, v << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or(row + k, v << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (sh + 2 * BITS > 32)
-      __hip_atomic_fetch_or(stage + k + 1, v >> (32 - sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_or(row + k + 1, v >> (32 - sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+
+// Codes, scale (and min) of one row straight to the cache: tile = start of
+// the token's 64-token tile in its plane, tt = the token's slot in it, srow
+// / mrow = its scale (min) entries; stage: 32 words of this wave's LDS.
+// Every lane executes every store (lanes sharing an address store the same
+// value), so no store sits on a branch.
+template <int BITS, int FAM>
+__device__ __forceinline__ void quantize_row_at(uint8_t *tile, int tt, uint16_t *srow, uint16_t *mrow,
+                                                float a, float c, uint32_t *stage) {
+  constexpr int RB = 16 * BITS;
+  constexpr int CK = chunk_bytes(RB);
+  const int lane = threadIdx.x & 63;
+  uint16_t dh, mh;
+  const uint32_t v = row_fields<BITS, FAM>(a, c, dh, mh);
+  srow[lane >> 4] = dh;
+  if constexpr (FAM == FAM_1) mrow[lane >> 4] = mh;
+  if constexpr (BITS == 8 || BITS == 4 || BITS == 2 || BITS == 1) {
+    constexpr int K = 16 / BITS;                   // lanes per dword
+    const uint32_t w = group_or<K>(v << (2 * BITS * (lane % K)));
+    const int byte = 4 * (lane / K);
+    *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = w;
+  } else {
+    constexpr int NW = RB / 4;
+    pack_row_lds<BITS>(v, stage);
     wave_sync();
-    if (lane < RB / 4) {
-      const int byte = 4 * lane;
-      *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = stage[lane];
-    }
+    const int wl = lane % NW;                      // lanes past NW repeat a word
+    const int byte = 4 * wl;
+    *reinterpret_cast<uint32_t *>(tile + ((byte / CK) * TILE + tt) * CK + byte % CK) = stage[wl];
     wave_sync();                                   // stage is free for the next item
   }
 }
 
-// Row of token t of codec CODEC (plain or KVarN plane; a, c = this lane's
-// stored coordinates 2l, 2l + 1).  stage: 32 words of this wave's LDS.
+// Row of token slot tt of a tile (codec CODEC, plain or KVarN plane; a, c =
+// this lane's stored coordinates 2l, 2l + 1).  stage: 32 words of this
+// wave's LDS.
 template <int CODEC>
-__device__ __forceinline__ void store_row(const PlaneArgs &p, long long rows, int t, float a, float c,
-                                          uint32_t *stage) {
+__device__ __forceinline__ void store_row_at(uint8_t *tile, int tt, uint16_t *srow, uint16_t *mrow, float a,
+                                             float c, uint32_t *stage) {
   const int lane = threadIdx.x & 63;
   if constexpr (CODEC == KVQ_F16) {
     // binary16 row: dword `lane` holds coordinates 2*lane, 2*lane+1
     const uint32_t pair = (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(c) << 16);
     const int byte = 4 * lane;
-    *reinterpret_cast<uint32_t *>(p.codes + rows * (2 * D) + tiled_offset(t, byte / 16, 2 * D, 16) +
-                                  byte % 16) = pair;
+    *reinterpret_cast<uint32_t *>(tile + ((byte / 16) * TILE + tt) * 16 + byte % 16) = pair;
   } else {
-    quantize_row<codec_bits(CODEC), codec_family(CODEC)>(p, rows, t, a, c, stage);
+    quantize_row_at<codec_bits(CODEC), codec_family(CODEC)>(tile, tt, srow, mrow, a, c, stage);
   }
+}
+
+// Row of token t of codec CODEC in the plane whose rows start at row `rows`
+// of the layer's planes.
+template <int CODEC, class PA>
+__device__ __forceinline__ void store_row(const PA &p, long long rows, int t, float a, float c,
+                                          uint32_t *stage) {
+  constexpr int RB = row_bytes(CODEC, D);
+  constexpr int NB = codec_family(CODEC) == FAM_F16 ? 0 : D / 32;
+  uint8_t *tile = p.codes + rows * RB + (long long)(t / TILE) * TILE * RB;
+  const long long so = (rows + t) * NB;
+  store_row_at<CODEC>(tile, t % TILE, p.scales + so, codec_family(CODEC) == FAM_1 ? p.mins + so : nullptr, a,
+                      c, stage);
 }
 
 // 16-bit tail copy (binary16 or bfloat16) of raw channels x of token t into
 // ring slot t mod tail_len of plane `plane` (= b * hkv + h).
-__device__ __forceinline__ void store_tail(const PlaneArgs &p, long long plane, int t, float2 x) {
+template <class PA>
+__device__ __forceinline__ void store_tail(const PA &p, long long plane, int t, float2 x) {
   const int lane = threadIdx.x & 63;
   const int slot = t % p.tail_len;
   const uint32_t pair =
@@ -156,7 +213,8 @@ __device__ __forceinline__ void store_tail(const PlaneArgs &p, long long plane, 
 
 // Stored coordinates of raw channels x of kv head h: x itself (plain), or
 // H (x * w) by the in-wave transform (KVarN).
-__device__ __forceinline__ void stored_coords(const PlaneArgs &p, int h, float2 x, float &a, float &c) {
+template <class PA>
+__device__ __forceinline__ void stored_coords(const PA &p, int h, float2 x, float &a, float &c) {
   const int lane = threadIdx.x & 63;
   a = x.x;
   c = x.y;
