@@ -2,8 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
-Sources: the KV-COBRA explainer defines bits per dimension (bpd) as the
-average number of bits spent per stored number, with F16 at 16 (Jargon), and
+Sources: the KV-COBRA explainer's jargon list defines bits per dimension
+(bpd) as the mean storage cost, in bits, of one stored coordinate (F16 is
+16), and
 its worked example ("Where the bits actually go") prices a head at
 ``rank * bits`` code bits per token against a budget of ``128 * bpd``.  The
 bandwidth thread's arithmetic (bytes read per generated token bound the

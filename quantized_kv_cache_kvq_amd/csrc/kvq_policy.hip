@@ -4,8 +4,9 @@
 //
 // The VBR announcement thread (opening posts) describes the behaviour: the
 // cache stays at 16 bits while it fits, then layers move down a codec
-// ladder one at a time in a profiled per-layer order ("F16 until 18k, then
-// F16/T8 mixes, and so on"), never below a floor codec (--vbr-floor), within
+// ladder one at a time in a profiled per-layer order (all layers at 16 bits
+// up to a context size, then mixes of 16-bit and lower-bit layers), never
+// below a floor codec (--vbr-floor), within
 // a VRAM budget (--vbr-vram); any added KV, injected or generated, can push a
 // degrade (the reply on injected KV).  Reading taken here: a degrade moves
 // one layer one rung; the next layer to move is the one at the highest rung
