@@ -608,21 +608,10 @@ kvq_status append_decode_impl(const kvq_layer *layer, const float *k_new, const 
                 layer->capacity);
   kvq_layer after = *layer;
   after.n_tokens = layer->n_tokens + 1;
-  const int G = n_q_heads > 0 && n_q_heads % layer->n_kv_heads == 0 ? n_q_heads / layer->n_kv_heads : 0;
-  const bool fused = G > 0 && decode_head_group(G) == G && layer->k.basis != KVQ_BASIS_LOWRANK;
-  if (fused)
-    return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, k_new, v_new, 1,
-                       check_only);
-  // not fusable here (several head groups per kv head read the same tiles,
-  // or low rank): the append launch, then the decode launch -- after the
-  // decode's own checks, so that an error enqueues nothing
-  s = decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, nullptr, nullptr, 1, true);
-  if (s != KVQ_OK || check_only) return s;
-  const PlaneArgs kp = plane_args(*layer, layer->k), vp = plane_args(*layer, layer->v);
-  hipError_t e = launch_append(kp, vp, k_new, v_new, layer->batch, 1, layer->n_tokens,
-                               layer->seq_tokens, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "append launch");
-  return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, nullptr, nullptr, 1);
+  // one launch: the workgroup whose tiles hold the new token writes its K
+  // and V rows (every head group's owner the same bytes) before reading
+  return decode_impl(after, q, n_q_heads, sm_scale, out, ws, ws_bytes, 0, stream, k_new, v_new, 1,
+                     check_only);
 }
 
 // Scratch of the allocation-free step: the decode workspace (completion

@@ -226,4 +226,129 @@ __device__ __forceinline__ void stored_coords(const PA &p, int h, float2 x, floa
   }
 }
 
+// Low-rank stored coordinates of one token: u = P^T x (P: 128 x 128
+// binary16, row c = input channel), lane l holding raw channels x = (2l,
+// 2l + 1) and getting nothing back: u lands in coords[0 .. 128).  xin,
+// coords: 128 floats of this wave's LDS each.  The wave reads all of P in
+// one round trip: load i of lane l is row 4i + l/16, columns 8(l%16) .. +8;
+// each lane sums its 8 columns over its 32 rows in row order, then the four
+// lanes holding the same columns (l, l^16, l^32, l^48) add their sums.
+__device__ inline void lr_project_row(const uint16_t *P, float2 x, float *xin, float *coords) {
+  const int lane = threadIdx.x & 63;
+  xin[2 * lane] = x.x;
+  xin[2 * lane + 1] = x.y;
+  wave_sync();
+  const u32x4 *P4 = reinterpret_cast<const u32x4 *>(P);
+  u32x4 pv[D / 4];
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) pv[i] = P4[64 * i + lane];
+  const int rsub = lane >> 4, c0 = 8 * (lane & 15);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) {
+    const float xr = xin[4 * i + rsub];
+    const uint32_t wv[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(f16_bits_to_f32((uint16_t)(wv[e] & 0xFFFFu)), xr, acc[2 * e]);
+      acc[2 * e + 1] = fmaf(f16_bits_to_f32((uint16_t)(wv[e] >> 16)), xr, acc[2 * e + 1]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16, 64);
+    acc[e] += __shfl_xor(acc[e], 32, 64);
+  }
+  if (rsub == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) coords[c0 + e] = acc[e];
+  }
+  wave_sync();
+}
+
+// Low-rank row of token t in plane geometry g: lane l holds stored
+// coordinates 2l, 2l+1 (v0, v1; lanes past the rank are ignored).  Block
+// scale (and min) per block of L = min(32, rank) coordinates, codes, packing
+// through pk (this wave's 128 bytes of LDS), store in the tiled layout.
+__device__ __forceinline__ void lr_store_row(const PlaneArgs &p, const HeadGeom &g, int t, float v0,
+                                             float v1, uint32_t *pk) {
+  const int lane = threadIdx.x & 63;
+  uint8_t *row_codes = p.codes + g.codes_off;
+  const int fam = codec_family(g.codec);
+  const int bits = codec_bits(g.codec);
+  // lane l holds stored coordinates 2l, 2l+1; block j (L = min(32, rank)
+  // coordinates) is lanes [j L/2, (j+1) L/2), reduced by shuffles within
+  // those aligned lane groups
+  const bool act = 2 * lane < g.n;
+  if (!act) v0 = v1 = 0.f;
+  const int half = g.L / 2;
+  const int j = lane / half, lead = j * half;
+  float d = 0.f, m = 0.f;
+  if (fam == FAM_0) {
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+    for (int o = half / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    const uint16_t dh = f32_to_f16_bits(amax / qmax);
+    if (act && lane == lead) p.scales[g.scales_off + (long long)t * g.nblk + j] = dh;
+    d = f16_bits_to_f32(dh);
+  } else {
+    float lo = act ? fminf(v0, v1) : __builtin_huge_valf(), hi = act ? fmaxf(v0, v1) : -__builtin_huge_valf();
+    for (int o = half / 2; o > 0; o >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    const uint16_t mh = f32_to_f16_bits(lo);
+    m = f16_bits_to_f32(mh);
+    const float levels = (float)((1 << bits) - 1);
+    const uint16_t dh = f32_to_f16_bits((hi - m) / levels);
+    if (act && lane == lead) {
+      const long long so = g.scales_off + (long long)t * g.nblk + j;
+      p.scales[so] = dh;
+      p.mins[so] = mh;
+    }
+    d = f16_bits_to_f32(dh);
+  }
+
+  // codes of the lane's two coordinates, OR-ed into the packed row in LDS
+  // (code e at bits [e b, e b + b) of the row)
+  if (lane < D / 4) pk[lane] = 0u;
+  wave_sync();
+  if (act) {
+    const uint32_t mask = (1u << bits) - 1u;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float x = k ? v1 : v0;
+      int q = 0;
+      if (fam == FAM_0) {
+        const float qmax = (float)((1 << (bits - 1)) - 1);
+        if (d != 0.f) q = (int)fminf(fmaxf(rintf(x / d), -qmax), qmax);
+      } else {
+        const float levels = (float)((1 << bits) - 1);
+        const float y = x - m;
+        if (d != 0.f) q = (int)fminf(fmaxf(rintf(y / d), 0.f), levels);
+      }
+      const uint32_t v = (uint32_t)q & mask;
+      const int bit = (2 * lane + k) * bits, wd = bit >> 5, sh = bit & 31;
+      __hip_atomic_fetch_or(pk + wd, v << sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+      if (sh + bits > 32)
+        __hip_atomic_fetch_or(pk + wd + 1, v >> (32 - sh), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    }
+  }
+  wave_sync();
+
+  // store: unit u (us bytes) is bytes [us u, us (u+1)) of the packed row
+  const int us = g.c < 4 ? g.c : 4;
+  const int nunits = g.R / us;
+  if (lane < nunits) {
+    const int byte = us * lane;
+    uint8_t *dst = row_codes + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c;
+    if (us == 4)
+      *reinterpret_cast<uint32_t *>(dst) = pk[lane];
+    else if (us == 2)
+      *reinterpret_cast<uint16_t *>(dst) = reinterpret_cast<const uint16_t *>(pk)[lane];
+    else
+      *dst = reinterpret_cast<const uint8_t *>(pk)[lane];
+  }
+}
+
 }  // namespace arow

@@ -57,65 +57,6 @@ __global__ __launch_bounds__(64) void query_prep_kernel(const float *__restrict_
   if ((lane & 15) == 0) qsum[(long long)bh * 4 + lane / 16] = sblk;
 }
 
-// Low-rank query projection q_low = P_g^T q on the matrix cores, scaled into
-// the log2 domain, plus per-block sums.  For kv head g the queries of its
-// G heads over all batch entries form M = B*G rows; the product
-// [M x 128] x [128 x r_g] runs as 16x16x4 fp32 MFMA tiles (fp32 inputs keep
-// the binary16 entries of P and the binary32 queries exact in the products).
-// One wave computes a 16-row by L-column tile (L = min(32, r_g): one block).
-__global__ __launch_bounds__(64) void lowrank_query_kernel(const float *__restrict__ q,
-                                                           PlaneArgs kp, int B, int Hq, int G,
-                                                           float scale, float *__restrict__ qw,
-                                                           float *__restrict__ qsum) {
-  const int g = blockIdx.z;
-  const int r = kp.hrank[g];
-  const int L = r < 32 ? r : 32;
-  const int jb = blockIdx.y;                 // block index along the rank
-  if (jb * L >= r) return;
-  const int m0 = blockIdx.x * 16;
-  const int M = B * G;
-  const int lane = threadIdx.x;
-  const int i_a = lane & 15, k_a = lane >> 4;
-  const uint16_t *P = kp.proj + (long long)g * D * D;
-
-  const int ma = m0 + i_a;
-  const float *qrow = nullptr;
-  if (ma < M) qrow = q + ((long long)(ma / G) * Hq + g * G + ma % G) * D;
-
-  // every load is issued before the products: the lane's 32 query values
-  // once, then per 16-column tile its 32 entries of P
-  float qa[D / 4];
-#pragma unroll
-  for (int i = 0; i < D / 4; ++i) qa[i] = qrow ? qrow[4 * i + k_a] : 0.f;
-  float rowsum[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int ct = 0; ct < L / 16; ++ct) {
-    const int n0 = jb * L + ct * 16;
-    uint16_t pb[D / 4];
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) pb[i] = P[(long long)(4 * i + k_a) * D + n0 + i_a];
-    floatx4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i)
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i], f16_bits_to_f32(pb[i]), c, 0, 0, 0);
-    // D[i][j]: lane holds rows 4*(lane/16) + rr, column lane % 16
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int m = m0 + 4 * (lane >> 4) + rr;
-      const float v = c[rr] * scale;
-      if (m < M) qw[((long long)(m / G) * Hq + g * G + m % G) * D + n0 + (lane & 15)] = v;
-      rowsum[rr] += v;
-    }
-  }
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    float v = rowsum[rr];
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    const int m = m0 + 4 * (lane >> 4) + rr;
-    if ((lane & 15) == 0 && m < M) qsum[((long long)(m / G) * Hq + g * G + m % G) * 4 + jb] = v;
-  }
-}
-
 // --------------------------------------------------------------- launcher --
 
 int decode_tile_tokens(int kcodec, int vcodec, int basis) {
@@ -227,12 +168,11 @@ hipError_t launch_decode(const DecodeArgs &args, const float *q, float sm_scale,
   DecodeArgs a = args;
   const float scale2 = sm_scale * LOG2E;
   if (a.k.basis == KVQ_BASIS_LOWRANK) {
-    dim3 g((a.B * a.G + 15) / 16, 4, a.Hkv);
-    hipLaunchKernelGGL(lowrank_query_kernel, g, dim3(64), 0, stream, q, a.k, a.B, a.Hq, a.G,
-                       scale2, qw, qsum);
-    a.q_body = qw;
+    // the body workgroups project the raw query themselves (P^T q on the
+    // matrix cores, before their first loads)
+    a.q_body = q;
     a.qsum = qsum;
-    a.scale_body = 1.f;
+    a.scale_body = scale2;
   } else if (prep) {
     hipLaunchKernelGGL(query_prep_kernel, dim3(a.B * a.Hq), dim3(64), 0, stream, q, a.k.w, a.Hq,
                        a.G, a.k.basis == KVQ_BASIS_HADAMARD ? 1 : 0, scale2, qw, qsum);

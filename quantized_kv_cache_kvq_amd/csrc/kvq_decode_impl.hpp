@@ -356,6 +356,7 @@ struct SplitIO {
   const uint8_t *kcodes; const uint16_t *ksc; const uint16_t *kmn;
   const uint8_t *vcodes; const uint16_t *vsc; const uint16_t *vmn;
   const float *q;              // HG query rows (stride 128), raw binary32
+  const float *q_lds;          // or (non-null) the rows in LDS, already in the log2 domain
   float scale;                 // multiplier into the log2 domain
   long long t_begin, t_end;    // token range (plane coordinates), t_begin % 64 == 0
   float *part;                 // partial row of head 0 of the group
@@ -491,7 +492,7 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const bool ok = h < HG && 8 * G + e < C::NK;
-      v[e] = ok ? io.q[h * D + 8 * G + e] * io.scale : 0.f;
+      v[e] = !ok ? 0.f : io.q_lds ? io.q_lds[h * D + 8 * G + e] : io.q[h * D + 8 * G + e] * io.scale;
       amax = fmaxf(amax, fabsf(v[e]));
     }
     amax = row_max16(amax);
@@ -856,6 +857,46 @@ __device__ __forceinline__ void seq_counts(const DecodeArgs &a, int b, int &body
   body = Tb - tail;
 }
 
+// Low-rank query coordinates of the group's HG heads: q'[h][n] = scale *
+// sum_c q[h][c] P[c][n] for n < rank, into LDS rows of 128 floats at q_out.
+// Wave w takes output columns 16w .. 16w + 15 on the matrix cores (binary32
+// 16x16x4: row = head, k = input channel 4i + lane/16 in row order), then
+// the workgroup waits for all of them.  Runs before the body's first loads;
+// the rows stay untouched until the producers of the query operands read
+// them (nothing writes LDS before that barrier).
+template <int HG>
+__device__ __forceinline__ void lr_query_project(const DecodeArgs &a, const float *q, int kvh, int rank,
+                                                 float *q_out) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (16 * w < rank) {
+    const int i_a = lane & 15, k_a = lane >> 4;
+    const uint16_t *P = a.k.proj + (long long)kvh * D * D;
+    const int n0 = 16 * w;
+    // rows past the group read head 0 (every load unconditional, so the
+    // products can start as operands arrive) and are zeroed before use
+    const bool live = i_a < HG;
+    const float *qr = q + (live ? i_a : 0) * D + k_a;
+    float qa[D / 4];
+    uint16_t pb[D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      qa[i] = qr[4 * i];
+      pb[i] = P[(4 * i + k_a) * D + n0 + i_a];
+    }
+    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(live ? qa[i] : 0.f, f16_bits_to_f32(pb[i]), c, 0, 0, 0);
+    // lane holds rows 4 (lane / 16) + rr of column lane % 16
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = 4 * k_a + rr;
+      if (h < HG) q_out[h * D + n0 + i_a] = c[rr] * a.scale_body;
+    }
+  }
+  __syncthreads();
+}
+
 // LR: per-head widths and codecs (low-rank planes, offsets from the head
 // tables); otherwise every plane has the configuration's fixed geometry.
 template <class C, bool LR>
@@ -880,7 +921,12 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, const Splits &sp, 
   io.vsc = a.v.scales ? a.v.scales + vso : nullptr;
   io.vmn = a.v.mins ? a.v.mins + vso : nullptr;
   io.q = a.q_body + ((long long)b * a.Hq + head0) * D;
+  io.q_lds = nullptr;
   io.scale = a.scale_body;
+  if constexpr (LR) {
+    lr_query_project<C::HG>(a, io.q, kvh, C::NK, reinterpret_cast<float *>(lds));
+    io.q_lds = reinterpret_cast<const float *>(lds);
+  }
   const long long tps = (long long)sp.tps * 64;
   io.t_begin = (long long)s * tps;
   io.t_end = io.t_begin + tps < a.body_tokens ? io.t_begin + tps : a.body_tokens;
@@ -908,6 +954,7 @@ __device__ __forceinline__ void run_tail(const DecodeArgs &a, const Splits &sp, 
   io.vcodes = reinterpret_cast<const uint8_t *>(a.v.tail) + plane * a.v.tail_len * (2 * D);
   io.ksc = io.kmn = io.vsc = io.vmn = nullptr;
   io.q = a.q_tail + ((long long)b * a.Hq + head0) * D;
+  io.q_lds = nullptr;
   io.scale = a.scale_tail;
   const long long tps = (long long)a.tps_tail * 64;
   io.t_begin = (long long)st * tps;
@@ -1113,6 +1160,42 @@ __device__ __forceinline__ void fused_append(const DecodeArgs &a, int b, int kvh
   __syncthreads();
 }
 
+// Low-rank layers: the new token's row of plane p (tail copy, u = P^T x,
+// the head's own width and codec), exactly as the append kernel's one-token
+// path stores it; this wave's 1280 bytes of LDS hold x, u and the packed row.
+__device__ __forceinline__ void fused_row_lr(const PlaneArgs &p, const float *x_new, const HeadGeom &g, int b,
+                                             int kvh, int t, uint8_t *lds) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long long plane = (long long)b * p.hkv + kvh;
+  const float2 x = reinterpret_cast<const float2 *>(x_new + plane * D)[lane];
+  if (p.tail_len > 0) arow::store_tail(p, plane, t, x);
+  float *xin = reinterpret_cast<float *>(lds + w * 1280), *coords = xin + D;
+  arow::lr_project_row(p.proj + (long long)kvh * D * D, x, xin, coords);
+  arow::lr_store_row(p, g, t, coords[2 * lane], coords[2 * lane + 1], reinterpret_cast<uint32_t *>(coords + D));
+}
+
+// The workgroup whose tiles hold the new token's position (the tail split
+// of its ring slot, else the body split of its row) writes its K and V rows
+// before any wave loads a tile.  With several head groups per kv head, the
+// owner of every group writes the same bytes.
+__device__ __forceinline__ void fused_append_lr(const DecodeArgs &a, const Splits &sp, int b, int kvh, int s,
+                                                bool tail, uint8_t *lds) {
+  int t = a.T - 1;
+  if (a.seq) {
+    const int sb = a.seq[b];
+    t = sb < 0 ? 0 : sb > a.T - 1 ? a.T - 1 : sb;
+  }
+  const bool mine = a.N > 0 ? tail && (s - sp.sb) == (t % a.N) / (a.tps_tail * 64)
+                            : !tail && s == t / (sp.tps * 64);
+  if (!mine) return;
+  const int w = threadIdx.x >> 6;
+  const HeadGeom g = lr_geom(a, b, kvh);
+  if (w == 0) fused_row_lr(a.k, a.k_new, g, b, kvh, t, lds);
+  else if (w == 1) fused_row_lr(a.v, a.v_new, g, b, kvh, t, lds);
+  __builtin_amdgcn_s_waitcnt(0);           // the rows are in L2 before any wave loads
+  __syncthreads();
+}
+
 template <int HG, int KC, int VC>
 __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_kernel(DecodeArgs a) {
   using CB = Cfg<HG, KC, VC, D, D>;
@@ -1166,6 +1249,7 @@ __global__ __launch_bounds__(WG, DECODE_WG_PER_CU) void decode_lowrank_kernel(De
   }
   const Splits sp = {lr_sbody(kvh), a.S_tail, lr_tps(kvh)};
   const int s = tail ? sp.sb + (x - a.lr_body_all - kvh * a.S_tail) : x - lr_first(kvh);
+  if (a.k_new) fused_append_lr(a, sp, b, kvh, s, tail, lds);
   if (tail) {
     if (a.k.tail_bf16) run_tail<HG, true>(a, sp, b, kvh, hg, s, lds);
     else run_tail<HG, false>(a, sp, b, kvh, hg, s, lds);

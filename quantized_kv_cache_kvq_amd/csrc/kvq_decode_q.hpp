@@ -201,8 +201,9 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   const int ph = 4 * wave + (lane >> 4), pG = lane & 15;   // producer: head, channel group
   float qv[8];
   if (producer && ph < HG && 8 * pG < Q::NK) {
-    const float4 x0 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(ph * D + 8 * pG));
-    const float4 x1 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(ph * D + 8 * pG + 4));
+    const float *qs = io.q_lds ? io.q_lds : io.q;
+    const float4 x0 = *reinterpret_cast<const float4 *>(qs + (unsigned)(ph * D + 8 * pG));
+    const float4 x1 = *reinterpret_cast<const float4 *>(qs + (unsigned)(ph * D + 8 * pG + 4));
     qv[0] = x0.x; qv[1] = x0.y; qv[2] = x0.z; qv[3] = x0.w;
     qv[4] = x1.x; qv[5] = x1.y; qv[6] = x1.z; qv[7] = x1.w;
   } else {
@@ -301,7 +302,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[e] = qv[grp8_perm<KB>(e)] * io.scale;
+      v[e] = io.q_lds ? qv[grp8_perm<KB>(e)] : qv[grp8_perm<KB>(e)] * io.scale;
       amax = fmaxf(amax, fabsf(v[e]));
     }
     amax = row_max16(amax);

@@ -11,8 +11,9 @@ takes one step; then
 Cases: the new token landing in the tail ring (T0 below, at and past the
 tail length, slot wrap), no tail (the new row read by the last body split),
 plain and KVarN bodies, 3/5/6-bit rows (LDS packing inside the launch),
-binary16 and bfloat16 tails, a ragged batch, and the two-launch path (two
-head groups per kv head; low rank)."""
+binary16 and bfloat16 tails, a ragged batch, two head groups per kv head
+(the owner workgroup of each group writes the same row), and low-rank
+layers (the launch projects and quantises the new rows and the query)."""
 
 import numpy as np
 import pytest
@@ -121,20 +122,76 @@ def test_step_matches_two_calls_and_oracle(gpu, name, kc, vc, Hq, T0, N, fmt, ra
     H.check_precision(outs[0], ref, bound, "%s %s/%s Hq=%d N=%d %s" % (name, kc, vc, Hq, N, fmt))
 
 
-def test_lowrank_step_two_launches(gpu):
-    wl = synth.WORKLOADS["lowrank_1bpd"].with_(B=2, T=301, N=0)
+LR_CASES = [
+    # Hq, T0, N, ragged
+    (32, 300, 0, False),      # the new row read by the last body split
+    (32, 127, 128, False),    # the new token in the tail ring, slot 127
+    (32, 300, 64, False),     # ring wrapped
+    (128, 200, 0, False),     # two head groups per kv head (both owners write the row)
+    (32, 150, 64, True),      # ragged batch
+]
+
+
+@pytest.mark.parametrize("Hq,T0,N,ragged", LR_CASES)
+def test_lowrank_step_one_launch(gpu, Hq, T0, N, ragged):
+    """Low-rank layer: the step's launch writes the new token's projected,
+    per-head-quantised rows and tail copy itself and projects the query in
+    its body workgroups.  Cache bytes and output equal the append + decode
+    calls bit for bit; the new rows follow the oracle under the tie rule;
+    the output matches the oracle's decode."""
+    B = 3 if ragged else 2
+    Ts = [T0 + 40, T0 + 3, T0] if ragged else [T0] * B
+    wl = synth.WORKLOADS["lowrank_1bpd"].with_(B=B, Hq=Hq, T=max(Ts) + 1, N=N)
     k = synth.layer_rows(wl, 0, "k").numpy()
     v = synth.layer_rows(wl, 0, "v").numpy()
     q = synth.queries(wl, 0)
     gk, gv, ok_, ov = H.specs(wl)
-    cache = H.new_cache(wl, 320, gk, gv, gpu, N=0)
-    _upload(cache, "k", k, ok_, [300, 300], 0, 320, "f16")
-    _upload(cache, "v", v, ov, [300, 300], 0, 320, "f16")
-    cache.n_tokens = 300
-    out = cache.append_decode(torch.from_numpy(k[:, 300:301].copy()).to(gpu),
-                              torch.from_numpy(v[:, 300:301].copy()).to(gpu), q.to(gpu), wl.sm_scale)
-    torch.cuda.synchronize()
-    ref = OL.decode(q.numpy(), OL.encode_plane(k, ok_), OL.encode_plane(v, ov), None, None, ok_, ov,
-                    301, 0, wl.sm_scale)
-    assert cache.n_tokens == 301
-    assert float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))) <= H.ATOL
+    cap = (max(Ts) + 1 + 63) // 64 * 64
+    kn = torch.from_numpy(np.stack([k[b, Ts[b]:Ts[b] + 1] for b in range(B)])).to(gpu)
+    vn = torch.from_numpy(np.stack([v[b, Ts[b]:Ts[b] + 1] for b in range(B)])).to(gpu)
+    outs, caches = [], []
+    for fused in (True, False):
+        c = _layer(wl, cap, gk, gv, gpu, N, "f16")
+        _upload(c, "k", k, ok_, Ts, N, cap, "f16")
+        _upload(c, "v", v, ov, Ts, N, cap, "f16")
+        c.n_tokens = max(Ts)
+        if ragged:
+            c.set_seq_tokens(torch.tensor(Ts, dtype=torch.int32, device=gpu))
+        if fused:
+            out = c.append_decode(kn, vn, q.to(gpu), wl.sm_scale)
+        else:
+            c.append(kn, vn)
+            out = c.decode(q.to(gpu), wl.sm_scale)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        caches.append(c)
+    assert np.array_equal(outs[0], outs[1]), "one-call step differs from append + decode"
+    T1 = [t + 1 for t in Ts]
+    for name_, x, spec in (("k", k, ok_), ("v", v, ov)):
+        d0, d1 = H.download(caches[0], name_), H.download(caches[1], name_)
+        for key in d0:
+            if d0[key] is not None:
+                assert np.array_equal(d0[key], d1[key]), (name_, key)
+        encs, _ = H.unpack(caches[0], name_, spec, max(T1))
+        mism = 0
+        for b in range(B):
+            for h in range(wl.Hkv):
+                e = {kk: (vv[T1[b] - 1:T1[b]] if isinstance(vv, np.ndarray) else vv) for kk, vv in encs[b][h].items()}
+                n, _ = H.check_rotated_head(x[b, T1[b] - 1:T1[b], h, :], e, spec, h, max_frac=1.0)
+                mism += n
+        assert mism <= 4, (name_, mism)
+        if N > 0:
+            ring = np.concatenate([OL.tail_ring(x[b:b + 1, :T1[b]], N) for b in range(B)])
+            assert np.array_equal(d0["tail"], OL.pack_tail(ring)), name_
+    ref = np.zeros(outs[0].shape)
+    bound = np.zeros(outs[0].shape)
+    for b in range(B):
+        kb, vb = k[b:b + 1, :T1[b]], v[b:b + 1, :T1[b]]
+        ke, ve = OL.encode_plane(kb, ok_), OL.encode_plane(vb, ov)
+        kt = OL.tail_ring(kb, N) if N else None
+        vt = OL.tail_ring(vb, N) if N else None
+        ref[b] = OL.decode(q.numpy()[b:b + 1], ke, ve, kt, vt, ok_, ov, T1[b], N, wl.sm_scale)[0]
+        bound[b] = H.decode_bound(q.numpy()[b:b + 1], ke, ve, kt, vt, ok_, ov, T1[b], N, wl.sm_scale)[0]
+    err = float(np.max(np.abs(outs[0].astype(np.float64) - ref)))
+    assert err <= H.ATOL, err
+    H.check_precision(outs[0], ref, bound, "lowrank Hq=%d T0=%d N=%d ragged=%s" % (Hq, T0, N, ragged))
