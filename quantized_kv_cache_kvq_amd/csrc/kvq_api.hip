@@ -224,18 +224,16 @@ int max_splits(const kvq_layer &L) {
 }
 
 struct WsLayout {
-  size_t cnt, qw, qsum, part, total;
+  size_t cnt, part, total;
 };
 
 // Workspace: split-completion counters (fixed size and place, zero between
-// calls), prepared query, per-block query sums, split partials.
+// calls), then the split partials.
 WsLayout ws_layout(const kvq_layer &L, int Hq, int S) {
   WsLayout w;
   const size_t bh = (size_t)L.batch * Hq;
   w.cnt = 0;
-  w.qw = align256(DECODE_CNT_BYTES);
-  w.qsum = w.qw + align256(bh * KVQ_HEAD_DIM * sizeof(float));
-  w.part = w.qsum + align256(bh * 4 * sizeof(float));
+  w.part = align256(DECODE_CNT_BYTES);
   w.total = w.part + align256(bh * (size_t)S * PSTRIDE * sizeof(float));
   return w;
 }
@@ -520,10 +518,6 @@ kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, fl
     P.S_body = smax;
   }
   P.S_total = P.S_body + P.S_tail;
-  // plain bodies need no query pre-transform (the kernel scales the raw
-  // query itself); KVarN bodies need the rotation
-  P.prep = L.k.basis == KVQ_BASIS_HADAMARD;
-  P.qsum = true;
 
   const WsLayout W = ws_layout(L, n_q_heads, P.S_total);
   if (!ws) return fail(KVQ_ERR_WORKSPACE, "workspace is NULL");
@@ -571,9 +565,7 @@ kvq_status decode_impl(const kvq_layer &L, const float *q, int32_t n_q_heads, fl
     a.lr_first[h] = (int16_t)a.lr_body_all;
     if (h < L.n_kv_heads) a.lr_body_all += lr_sb[h];
   }
-  hipError_t e = launch_decode(a, q, sm_scale, reinterpret_cast<float *>(wsb + W.qw),
-                               reinterpret_cast<float *>(wsb + W.qsum), out,
-                               reinterpret_cast<hipStream_t>(stream), P.prep, P.qsum);
+  hipError_t e = launch_decode(a, q, sm_scale, out, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
@@ -615,7 +607,7 @@ kvq_status append_decode_impl(const kvq_layer *layer, const float *k_new, const 
 }
 
 // Scratch of the allocation-free step: the decode workspace (completion
-// counters, prepared query, split partials) in a fixed device array.  Each
+// counters and split partials) in a fixed device array.  Each
 // GPU the library runs on holds its own copy for the life of the process;
 // host code reaches it only through the address hipGetSymbolAddress gives
 // on that device.

@@ -1,6 +1,6 @@
-// Decode attention over the packed cache: query pre-transforms, the launch
-// of the split-K decode kernel (kvq_decode_impl.hpp, kvq_decode_q.hpp) and
-// its event-timing hook.
+// Decode attention over the packed cache: the launch of the split-K decode
+// kernel (kvq_decode_impl.hpp, kvq_decode_q.hpp; KVarN and low-rank body
+// workgroups transform the raw query themselves) and its event-timing hook.
 //
 // The computation (forum thread on decode bandwidth, second post): scores
 // s_t = sm_scale <q, k_t>, softmax over t, output sum_t p_t v_t; the cache is
@@ -16,46 +16,6 @@
 #include "kvq_decode_impl.hpp"
 
 namespace kvq {
-
-// --------------------------------------------------- query pre-transforms --
-
-// KVarN query: q' = H (q / w_k) / 128, scaled into the log2 domain; plain
-// bodies with _1 keys only get the scaling.  Also the per-32-block sums of q'
-// for _1 keys.  One wave per (batch entry, query head).
-__global__ __launch_bounds__(64) void query_prep_kernel(const float *__restrict__ q,
-                                                        const float *__restrict__ wk, int Hq,
-                                                        int G, int hadamard, float scale,
-                                                        float *__restrict__ qw,
-                                                        float *__restrict__ qsum) {
-  const int bh = blockIdx.x;
-  const int h = bh % Hq;
-  const int g = h / G;
-  const int lane = threadIdx.x;
-  float2 x = reinterpret_cast<const float2 *>(q + (long long)bh * D)[lane];
-  if (hadamard) {
-    const float *w = wk + (long long)g * D;
-    float a = x.x / w[2 * lane], b = x.y / w[2 * lane + 1];
-    float s0 = a + b, d0 = a - b;
-    a = s0;
-    b = d0;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      float pa = __shfl_xor(a, m, 64), pb = __shfl_xor(b, m, 64);
-      bool upper = (lane & m) != 0;
-      a = upper ? (pa - a) : (a + pa);
-      b = upper ? (pb - b) : (b + pb);
-    }
-    x.x = a * (1.f / 128.f);
-    x.y = b * (1.f / 128.f);
-  }
-  x.x *= scale;
-  x.y *= scale;
-  reinterpret_cast<float2 *>(qw + (long long)bh * D)[lane] = x;
-  float sblk = x.x + x.y;
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) sblk += __shfl_xor(sblk, o, 64);
-  if ((lane & 15) == 0) qsum[(long long)bh * 4 + lane / 16] = sblk;
-}
 
 // --------------------------------------------------------------- launcher --
 
@@ -163,28 +123,14 @@ hipError_t timing_end(double *total_ms, int *count) {
   return err;
 }
 
-hipError_t launch_decode(const DecodeArgs &args, const float *q, float sm_scale, float *qw,
-                         float *qsum, float *out, hipStream_t stream, bool prep, bool need_qsum) {
+hipError_t launch_decode(const DecodeArgs &args, const float *q, float sm_scale, float *out,
+                         hipStream_t stream) {
   DecodeArgs a = args;
   const float scale2 = sm_scale * LOG2E;
-  if (a.k.basis == KVQ_BASIS_LOWRANK) {
-    // the body workgroups project the raw query themselves (P^T q on the
-    // matrix cores, before their first loads)
-    a.q_body = q;
-    a.qsum = qsum;
-    a.scale_body = scale2;
-  } else if (prep) {
-    hipLaunchKernelGGL(query_prep_kernel, dim3(a.B * a.Hq), dim3(64), 0, stream, q, a.k.w, a.Hq,
-                       a.G, a.k.basis == KVQ_BASIS_HADAMARD ? 1 : 0, scale2, qw, qsum);
-    a.q_body = qw;
-    a.qsum = qsum;
-    a.scale_body = 1.f;
-  } else {
-    a.q_body = q;
-    a.qsum = qsum;
-    a.scale_body = scale2;
-  }
-  (void)need_qsum;
+  // plain bodies scale the raw query themselves; KVarN and low-rank body
+  // workgroups transform it first (rotation / projection), into LDS
+  a.q_body = q;
+  a.scale_body = scale2;
   a.q_tail = q;
   a.scale_tail = scale2;
   hipError_t e = hipGetLastError();

@@ -356,13 +356,46 @@ struct SplitIO {
   const uint8_t *kcodes; const uint16_t *ksc; const uint16_t *kmn;
   const uint8_t *vcodes; const uint16_t *vsc; const uint16_t *vmn;
   const float *q;              // HG query rows (stride 128), raw binary32
-  const float *q_lds;          // or (non-null) the rows in LDS, already in the log2 domain
+  const float *rot_w;          // KVarN body: the kv head's vector w (the query is rotated), else null
   float scale;                 // multiplier into the log2 domain
   long long t_begin, t_end;    // token range (plane coordinates), t_begin % 64 == 0
   float *part;                 // partial row of head 0 of the group
   long long part_head_stride;  // floats between consecutive heads' partials
   int dyn;                     // integer path: waves claim tiles past their first at run time
 };
+
+// KVarN query rotation in the producers' layout: the 16 lanes of a DPP row
+// hold one head, lane g channels 8g .. 8g + 7.  q' = H (q / w) / 128 with
+// the butterflies (u, v) -> (u + v, u - v) in increasing stride: strides
+// 1, 2, 4 inside the lane, then 8 .. 64 with the partner lane g ^ 1 .. g ^ 8.
+// All 16 lanes of a row take part (rows of absent heads hold zeros).
+__device__ __forceinline__ void rotate_row8(float (&x)[8], const float *w, int g) {
+  const float4 w0 = reinterpret_cast<const float4 *>(w)[2 * g], w1 = reinterpret_cast<const float4 *>(w)[2 * g + 1];
+  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = x[e] / wv[e];
+#pragma unroll
+  for (int st = 1; st < 8; st <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e & st) continue;
+      const float u = x[e], v = x[e + st];
+      x[e] = u + v;
+      x[e + st] = u - v;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const bool upper = (g & m) != 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __shfl_xor(x[e], m, 64);
+      x[e] = upper ? (p - x[e]) : (x[e] + p);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= 1.f / 128.f;
+}
 
 __device__ __forceinline__ uint2 side_raw(const uint16_t *base, long long t, bool valid, int nb) {
   if (!valid) return make_uint2(0u, 0u);
@@ -490,9 +523,11 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
     float v[8];
     float amax = 0.f;
 #pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = h < HG && 8 * G + e < C::NK ? io.q[h * D + 8 * G + e] : 0.f;
+    if (io.rot_w) rotate_row8(v, io.rot_w, G);
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const bool ok = h < HG && 8 * G + e < C::NK;
-      v[e] = !ok ? 0.f : io.q_lds ? io.q_lds[h * D + 8 * G + e] : io.q[h * D + 8 * G + e] * io.scale;
+      v[e] *= io.scale;
       amax = fmaxf(amax, fabsf(v[e]));
     }
     amax = row_max16(amax);
@@ -921,12 +956,9 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, const Splits &sp, 
   io.vsc = a.v.scales ? a.v.scales + vso : nullptr;
   io.vmn = a.v.mins ? a.v.mins + vso : nullptr;
   io.q = a.q_body + ((long long)b * a.Hq + head0) * D;
-  io.q_lds = nullptr;
   io.scale = a.scale_body;
-  if constexpr (LR) {
-    lr_query_project<C::HG>(a, io.q, kvh, C::NK, reinterpret_cast<float *>(lds));
-    io.q_lds = reinterpret_cast<const float *>(lds);
-  }
+  io.rot_w = !LR && a.k.basis == KVQ_BASIS_HADAMARD ? a.k.w + (long long)kvh * D : nullptr;
+  if constexpr (LR) lr_query_project<C::HG>(a, io.q, kvh, C::NK, reinterpret_cast<float *>(lds));
   const long long tps = (long long)sp.tps * 64;
   io.t_begin = (long long)s * tps;
   io.t_end = io.t_begin + tps < a.body_tokens ? io.t_begin + tps : a.body_tokens;
@@ -938,7 +970,7 @@ __device__ __forceinline__ void run_body(const DecodeArgs &a, const Splits &sp, 
   io.part = a.part + (((long long)b * a.Hq + head0) * a.S_total + s) * PSTRIDE;
   io.part_head_stride = (long long)a.S_total * PSTRIDE;
   io.dyn = sp.tps >= DYN_TILES_PER_WAVE * NWAVE;
-  if constexpr (BodyLds<C>::INT_QK) attend_q<C>(io, lds);
+  if constexpr (BodyLds<C>::INT_QK) attend_q<C, LR>(io, lds);
   else attend_range<C>(io, lds);
 }
 
@@ -954,7 +986,7 @@ __device__ __forceinline__ void run_tail(const DecodeArgs &a, const Splits &sp, 
   io.vcodes = reinterpret_cast<const uint8_t *>(a.v.tail) + plane * a.v.tail_len * (2 * D);
   io.ksc = io.kmn = io.vsc = io.vmn = nullptr;
   io.q = a.q_tail + ((long long)b * a.Hq + head0) * D;
-  io.q_lds = nullptr;
+  io.rot_w = nullptr;
   io.scale = a.scale_tail;
   const long long tps = (long long)a.tps_tail * 64;
   io.t_begin = (long long)st * tps;

@@ -169,7 +169,10 @@ __device__ __forceinline__ uint64_t kq_load(const uint8_t *__restrict__ tile, in
   return live ? w : 0;
 }
 
-template <class C>
+// QL: the group's query rows sit at the start of LDS, already in the log2
+// domain (low-rank bodies project them there); else io.q (raw, rotated here
+// when io.rot_w is set).
+template <class C, bool QL>
 __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   using Q = QCfg<C>;
   constexpr int HG = Q::HG, TT = Q::TT, NT = Q::NT, NKB = Q::NKB, NBV = Q::NBV, NDT = Q::NDT;
@@ -201,9 +204,14 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   const int ph = 4 * wave + (lane >> 4), pG = lane & 15;   // producer: head, channel group
   float qv[8];
   if (producer && ph < HG && 8 * pG < Q::NK) {
-    const float *qs = io.q_lds ? io.q_lds : io.q;
-    const float4 x0 = *reinterpret_cast<const float4 *>(qs + (unsigned)(ph * D + 8 * pG));
-    const float4 x1 = *reinterpret_cast<const float4 *>(qs + (unsigned)(ph * D + 8 * pG + 4));
+    float4 x0, x1;
+    if constexpr (QL) {
+      x0 = reinterpret_cast<const float4 *>(lds)[(ph * D + 8 * pG) / 4];
+      x1 = reinterpret_cast<const float4 *>(lds)[(ph * D + 8 * pG + 4) / 4];
+    } else {
+      x0 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(ph * D + 8 * pG));
+      x1 = *reinterpret_cast<const float4 *>(io.q + (unsigned)(ph * D + 8 * pG + 4));
+    }
     qv[0] = x0.x; qv[1] = x0.y; qv[2] = x0.z; qv[3] = x0.w;
     qv[4] = x1.x; qv[5] = x1.y; qv[6] = x1.z; qv[7] = x1.w;
   } else {
@@ -300,9 +308,10 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     const int hh = lane >> 4, j = pG >> 2, gk = pG & 3;
     float v[8];
     float amax = 0.f;
+    if (!QL && io.rot_w) rotate_row8(qv, io.rot_w, pG);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      v[e] = io.q_lds ? qv[grp8_perm<KB>(e)] : qv[grp8_perm<KB>(e)] * io.scale;
+      v[e] = QL ? qv[grp8_perm<KB>(e)] : qv[grp8_perm<KB>(e)] * io.scale;
       amax = fmaxf(amax, fabsf(v[e]));
     }
     amax = row_max16(amax);

@@ -15,8 +15,6 @@ struct DecodePlan {
   int tt_body;                    // tokens per workgroup tile of the body
   int S_body, S_tail, S_total;    // context splits per (b, kv head, head group)
   int tiles_per_split_body, tiles_per_split_tail;
-  bool prep;                      // query pre-transform needed
-  bool qsum;                      // per-block query sums needed (_1 keys)
 };
 
 // Kernel arguments of the split-K decode.  The scalars and pointers every
@@ -32,9 +30,8 @@ struct DecodeArgs {
   int tt_body;
   float scale_body;               // multiplier taking body scores to the log2 domain
   float scale_tail;
-  const float *q_body;    // [B][Hq][128] (raw query, or pre-transformed)
+  const float *q_body;    // [B][Hq][128] raw query (KVarN / low-rank bodies transform it in LDS)
   const float *q_tail;    // [B][Hq][128] raw query
-  const float *qsum;      // [B][Hq][4] per-block query sums (_1 keys)
   float *part;            // [B][Hq][S_total][PSTRIDE]
   float *out;             // [B][Hq][128] final output
   unsigned *cnt;          // [B][Hkv][NHG] finished-split counters (zero between calls)
@@ -63,8 +60,8 @@ hipError_t launch_dequant(const PlaneArgs &p, int batch, int T, const int32_t *s
 hipError_t launch_transcode(const PlaneArgs &src, const PlaneArgs &dst, int batch, int T,
                             hipStream_t stream);
 
-hipError_t launch_decode(const DecodeArgs &a, const float *q, float sm_scale, float *qw,
-                         float *qsum, float *out, hipStream_t stream, bool prep, bool need_qsum);
+hipError_t launch_decode(const DecodeArgs &a, const float *q, float sm_scale, float *out,
+                         hipStream_t stream);
 
 // Status with detail for kvq_last_error (host).
 kvq_status api_fail(kvq_status s, const char *detail);
