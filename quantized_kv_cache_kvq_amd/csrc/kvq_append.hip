@@ -375,16 +375,18 @@ __global__ __launch_bounds__(AF_THREADS) void append_flat_kernel(PlaneArgs kp, P
 }
 
 // Low-rank planes, prefill-sized appends: u = P_h^T x for 16 tokens at a
-// time on the matrix cores (v_mfma_f32_16x16x32_f16), so P_h is read once
-// per 64 tokens instead of once per token.  A workgroup of 4 waves takes 64
-// consecutive new tokens of one (K|V, batch entry, kv head); P_h (binary16,
-// exact) is staged in LDS once and read back transposed as the B operand;
-// each wave's A operand is its 16 token rows split into binary16 hi + lo
-// parts (x = hi + lo to ~22 bits; both products are exact and accumulate in
-// binary32).  The 16 x rank result goes through LDS to one row per pass of
-// lr_store_row, the same quantiser as the one-token path.
+// time on the matrix cores (v_mfma_f32_16x16x32_f16).  A workgroup of 4
+// waves takes LRM_CHUNKS runs of 64 consecutive new tokens of one (K|V,
+// batch entry, kv head); P_h (binary16, exact) is staged in LDS once and
+// read back transposed as the B operand; each wave's A operand is its 16
+// token rows split into binary16 hi + lo parts (x = hi + lo to ~22 bits;
+// both products are exact and accumulate in binary32).  The 16 x rank
+// result goes through LDS; then lane (token r, block j) quantises block j of
+// token r on its own (the formulas of the one-token path, so the same codes
+// for the same u) and stores the block's field, scale and min.
 constexpr int LRM_WAVES = 4;
 constexpr int LRM_ROWS = 16;                    // tokens per wave
+constexpr int LRM_CHUNKS = 16;                  // 64-token runs per workgroup
 constexpr int LRM_PPITCH = 2 * D + 32;          // staged P row (bytes)
 constexpr int LRM_UPITCH = D + 4;               // staged result row (floats)
 
@@ -402,15 +404,96 @@ __device__ __forceinline__ lrm_half8 lrm_tr16(const uint8_t *p0, const uint8_t *
   return __builtin_bit_cast(lrm_half8, v);
 }
 
-// One (plane, batch entry b, kv head h, 64-token chunk); p is bound at the
-// call site (a run-time choice between the two plane arguments would copy
-// them to scratch).
-__device__ __forceinline__ void lowrank_chunk(const PlaneArgs &p, const float *__restrict__ src, int b,
-                                              int h, int n_new, int tb, uint8_t *pl, float *ul,
-                                              uint32_t *pk) {
+// Block j (L = g.L coordinates ub[0 .. L) of token t) of a low-rank row of
+// BITS-bit codes: scale (and min), codes as in the one-token path, and the
+// block's field (code e at bit e * BITS, L * BITS / 8 bytes at row byte
+// j * L * BITS / 8), stored in the tiled layout.
+template <int BITS>
+__device__ __forceinline__ void lr_block_store(const PlaneArgs &p, const HeadGeom &g, int t, int j,
+                                               const float *ub) {
+  const int L = g.L;
+  const bool f0 = codec_family(g.codec) == FAM_0;
+  const long long so = g.scales_off + (long long)t * g.nblk + j;
+  float x[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) x[e] = e < L ? ub[e] : 0.f;
+  float d, m = 0.f;
+  if (f0) {
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+    const uint16_t dh = f32_to_f16_bits(amax / qmax);
+    p.scales[so] = dh;
+    d = f16_bits_to_f32(dh);
+  } else {
+    float lo = x[0], hi = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e)
+      if (e < L) {
+        lo = fminf(lo, x[e]);
+        hi = fmaxf(hi, x[e]);
+      }
+    const uint16_t mh = f32_to_f16_bits(lo);
+    m = f16_bits_to_f32(mh);
+    constexpr float levels = (float)((1 << BITS) - 1);
+    const uint16_t dh = f32_to_f16_bits((hi - m) / levels);
+    p.scales[so] = dh;
+    p.mins[so] = mh;
+    d = f16_bits_to_f32(dh);
+  }
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  uint32_t w[BITS];
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) w[k] = 0u;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    uint32_t q = 0u;
+    if (d != 0.f && e < L) {
+      if (f0) {
+        constexpr float qmax = (float)((1 << (BITS - 1)) - 1);
+        q = (uint32_t)(int)fminf(fmaxf(rintf(x[e] / d), -qmax), qmax) & mask;
+      } else {
+        constexpr float levels = (float)((1 << BITS) - 1);
+        q = (uint32_t)(int)fminf(fmaxf(rintf((x[e] - m) / d), 0.f), levels);
+      }
+    }
+    const int bit = e * BITS;
+    w[bit >> 5] |= q << (bit & 31);
+    if ((bit & 31) + BITS > 32) w[(bit >> 5) + 1] |= q >> (32 - (bit & 31));
+  }
+  // the field in units no wider than the layout's chunk: dwords when
+  // chunks hold 4+ bytes (then the field is whole dwords), else 16-bit
+  // halves (rows of 2, 6 or 10 bytes: rank 16 at 1, 3 or 5 bits)
+  uint8_t *row = p.codes + g.codes_off;
+  const int fbytes = L * BITS / 8, fb = j * fbytes;
+  if (g.c >= 4) {
+#pragma unroll
+    for (int k = 0; k < BITS; ++k)
+      if (4 * k < fbytes) {
+        const int byte = fb + 4 * k;
+        *reinterpret_cast<uint32_t *>(row + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c) = w[k];
+      }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2 * BITS; ++k)
+      if (2 * k < fbytes) {
+        const int byte = fb + 2 * k;
+        *reinterpret_cast<uint16_t *>(row + tiled_offset(t, byte / g.c, g.R, g.c) + byte % g.c) =
+            (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+      }
+  }
+}
+
+// LRM_CHUNKS runs of 64 tokens of one (plane, batch entry b, kv head h) whose
+// codes have BITS bits (one quantiser per instantiation keeps the loop's
+// registers low); p is bound at the call site (a run-time choice between
+// the two plane arguments would copy them to scratch).
+template <int BITS>
+__device__ __forceinline__ void lowrank_runs(const PlaneArgs &p, const float *__restrict__ src, int b,
+                                             int h, int n_new, int tb, uint8_t *pl, float *ul) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hkv = p.hkv;
-  const int i0 = (int)blockIdx.x * (LRM_WAVES * LRM_ROWS) + w * LRM_ROWS;   // this wave's first token
 
   // stage P_h: row c (input channel) at c * LRM_PPITCH, 256 bytes each
   {
@@ -421,57 +504,84 @@ __device__ __forceinline__ void lowrank_chunk(const PlaneArgs &p, const float *_
     }
   }
   __syncthreads();
-  if (i0 >= n_new) return;
-
-  // A operand: row r = lane % 16 is token i0 + r (rows past n_new repeat
-  // the last token and are not stored), k-group kg = lane / 16
-  const int r = lane & 15, kg = lane >> 4;
-  const int ir = i0 + r < n_new ? i0 + r : n_new - 1;
-  const float *xr = src + (((long long)b * n_new + ir) * hkv + h) * D;
-  lrm_half8 ahi[D / 32], alo[D / 32];
-#pragma unroll
-  for (int kc = 0; kc < D / 32; ++kc) {
-    const float4 x0 = *reinterpret_cast<const float4 *>(xr + 32 * kc + 8 * kg);
-    const float4 x1 = *reinterpret_cast<const float4 *>(xr + 32 * kc + 8 * kg + 4);
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const _Float16 hi = (_Float16)xs[e];
-      ahi[kc][e] = hi;
-      alo[kc][e] = (_Float16)(xs[e] - (float)hi);
-    }
-  }
   const HeadGeom g = head_geom(p, b, h);
+  const long long plane = (long long)b * hkv + h;
   float *u = ul + w * (LRM_ROWS * LRM_UPITCH);
-  for (int ct = 0; ct < (g.n + 15) / 16; ++ct) {
-    lrm_floatx4 c = {0.f, 0.f, 0.f, 0.f};
+  const int r = lane & 15, kg = lane >> 4;
+  // A operand: row r is token i0 + r of this wave's run (rows past n_new
+  // repeat the last token and are not stored), k-group kg; lane (r, kg)
+  // holds channels 32 kc + 8 kg .. + 8 of its token.  The next run's rows
+  // load while this run is projected and stored (the loads are
+  // unconditional, clamped into the input, so the wait for them is exact).
+  const int run0 = (int)blockIdx.x * LRM_CHUNKS * (LRM_WAVES * LRM_ROWS) + w * LRM_ROWS;
+  if (run0 >= n_new) return;
+  float xv[D / 4];
+#define KVQ_LRM_LOAD_ROWS(I0)                                                                      \
+  {                                                                                                \
+    const int ir_ = (I0) + r < n_new ? (I0) + r : n_new - 1;                                       \
+    const float *xr_ = src + (((long long)b * n_new + ir_) * hkv + h) * D;                         \
+    _Pragma("unroll") for (int kc = 0; kc < D / 32; ++kc) {                                        \
+      const float4 x0 = *reinterpret_cast<const float4 *>(xr_ + 32 * kc + 8 * kg);                 \
+      const float4 x1 = *reinterpret_cast<const float4 *>(xr_ + 32 * kc + 8 * kg + 4);             \
+      xv[8 * kc] = x0.x; xv[8 * kc + 1] = x0.y; xv[8 * kc + 2] = x0.z; xv[8 * kc + 3] = x0.w;      \
+      xv[8 * kc + 4] = x1.x; xv[8 * kc + 5] = x1.y; xv[8 * kc + 6] = x1.z; xv[8 * kc + 7] = x1.w;  \
+    }                                                                                              \
+  }
+  KVQ_LRM_LOAD_ROWS(run0)
+  for (int ch = 0;; ++ch) {
+    const int i0 = run0 + ch * (LRM_WAVES * LRM_ROWS);
+    // precision tail of the newest tail_len tokens: the lane's 4 chunks of
+    // 8 channels, 16 bytes each
+    const int ti = i0 + r, tt = tb + ti;
+    const bool row_ok = ti < n_new && (unsigned)tt < (unsigned)p.capacity;
+    if (row_ok && p.tail_len > 0 && ti + p.tail_len >= n_new) {
+      const int slot = tt % p.tail_len;
+      uint8_t *base = reinterpret_cast<uint8_t *>(p.tail) + plane * p.tail_len * (2 * D);
+#pragma unroll
+      for (int kc = 0; kc < D / 32; ++kc) {
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = xv[8 * kc + 2 * e], hi = xv[8 * kc + 2 * e + 1];
+          v[e] = p.tail_bf16 ? (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16)
+                             : (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+        }
+        *reinterpret_cast<u32x4 *>(base + tiled_offset(slot, 4 * kc + kg, 2 * D, 16)) = v;
+      }
+    }
+    lrm_half8 ahi[D / 32], alo[D / 32];
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc) {
-      // column n = lane % 16 of tile ct, rows 32kc + 8kg .. +7
-      const uint8_t *pb = pl + (32 * kc + 8 * kg + (r >> 2)) * LRM_PPITCH + (16 * ct + 4 * (r & 3)) * 2;
-      const lrm_half8 bv = lrm_tr16(pb, pb + 4 * LRM_PPITCH);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kc], bv, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kc], bv, c, 0, 0, 0);
-    }
-    // lane (n, g) holds rows 4g .. 4g+3 of column n
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) u[(4 * kg + rr) * LRM_UPITCH + 16 * ct + r] = c[rr];
-  }
-  wave_sync();
-
-  const long long plane = (long long)b * hkv + h;
-  for (int rr = 0; rr < LRM_ROWS; ++rr) {
-    const int i = i0 + rr;
-    if (i >= n_new) break;
-    const int t = tb + i;
-    if ((unsigned)t >= (unsigned)p.capacity) continue;   // ragged position out of contract
-    if (p.tail_len > 0 && i + p.tail_len >= n_new) {
-      const float2 x = reinterpret_cast<const float2 *>(src + (((long long)b * n_new + i) * hkv + h) * D)[lane];
-      store_tail(p, plane, t, x);
+      for (int e = 0; e < 8; ++e) {
+        const _Float16 hi = (_Float16)xv[8 * kc + e];
+        ahi[kc][e] = hi;
+        alo[kc][e] = (_Float16)(xv[8 * kc + e] - (float)hi);
+      }
     }
-    const float2 uv = *reinterpret_cast<const float2 *>(u + rr * LRM_UPITCH + 2 * lane);
-    lr_store_row(p, g, t, uv.x, uv.y, pk + w * (D / 4));
+    const bool more = ch + 1 < LRM_CHUNKS && i0 + LRM_WAVES * LRM_ROWS < n_new;
+    KVQ_LRM_LOAD_ROWS(more ? i0 + LRM_WAVES * LRM_ROWS : i0)
+    for (int ct = 0; ct < (g.n + 15) / 16; ++ct) {
+      lrm_floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < D / 32; ++kc) {
+        // column n = lane % 16 of tile ct, rows 32kc + 8kg .. +7
+        const uint8_t *pb = pl + (32 * kc + 8 * kg + (r >> 2)) * LRM_PPITCH + (16 * ct + 4 * (r & 3)) * 2;
+        const lrm_half8 bv = lrm_tr16(pb, pb + 4 * LRM_PPITCH);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kc], bv, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kc], bv, c, 0, 0, 0);
+      }
+      // lane (n, g) holds rows 4g .. 4g+3 of column n
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) u[(4 * kg + rr) * LRM_UPITCH + 16 * ct + r] = c[rr];
+    }
+    wave_sync();
+    // lane (token r, block j = kg) quantises and stores its block
+    if (row_ok && kg < g.nblk) lr_block_store<BITS>(p, g, tt, kg, u + r * LRM_UPITCH + kg * g.L);
+    wave_sync();                                   // u is free for the next run
+    if (!more) break;
   }
+#undef KVQ_LRM_LOAD_ROWS
 }
 
 __global__ __launch_bounds__(64 * LRM_WAVES) void append_lowrank_kernel(PlaneArgs kp, PlaneArgs vp,
@@ -481,14 +591,21 @@ __global__ __launch_bounds__(64 * LRM_WAVES) void append_lowrank_kernel(PlaneArg
                                                                          const int32_t *__restrict__ seq) {
   __shared__ __attribute__((aligned(16))) uint8_t pl[D * LRM_PPITCH];
   __shared__ __attribute__((aligned(16))) float ul[LRM_WAVES * LRM_ROWS * LRM_UPITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t pk[LRM_WAVES * (D / 4)];
-  // grid: x = 64-token chunk, y = kv head, z = K|V * batch + b
+  // grid: x = run of LRM_CHUNKS x 64 tokens, y = kv head, z = K|V * batch + b
   const int which = (int)blockIdx.z / batch, b = (int)blockIdx.z % batch, h = (int)blockIdx.y;
   const int tb = seq ? __builtin_amdgcn_readfirstlane(seq[b]) : t0;
-  if (which)
-    lowrank_chunk(vp, v_new, b, h, n_new, tb, pl, ul, pk);
-  else
-    lowrank_chunk(kp, k_new, b, h, n_new, tb, pl, ul, pk);
+  // the head's code width (K and V share it), one loop per width
+  switch (codec_bits(kp.hcodec[h])) {
+#define KVQ_LRM_CASE(BB)                                       \
+  case BB:                                                     \
+    if (which) lowrank_runs<BB>(vp, v_new, b, h, n_new, tb, pl, ul); \
+    else lowrank_runs<BB>(kp, k_new, b, h, n_new, tb, pl, ul);      \
+    break;
+    KVQ_LRM_CASE(1) KVQ_LRM_CASE(2) KVQ_LRM_CASE(3) KVQ_LRM_CASE(4) KVQ_LRM_CASE(5) KVQ_LRM_CASE(6)
+    KVQ_LRM_CASE(8)
+#undef KVQ_LRM_CASE
+    default: break;
+  }
 }
 
 hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *k_new,
@@ -500,7 +617,7 @@ hipError_t launch_append(const PlaneArgs &kp, const PlaneArgs &vp, const float *
   long long blocks = (items + AP_WAVES - 1) / AP_WAVES;
   if (blocks > 1024) blocks = 1024;
   if (kp.basis == KVQ_BASIS_LOWRANK && vp.basis == KVQ_BASIS_LOWRANK && n_new >= LRM_ROWS) {
-    const int per = LRM_WAVES * LRM_ROWS;
+    const int per = LRM_CHUNKS * LRM_WAVES * LRM_ROWS;
     const dim3 grid((unsigned)((n_new + per - 1) / per), (unsigned)kp.hkv, (unsigned)(2 * batch));
     hipLaunchKernelGGL(append_lowrank_kernel, grid, dim3(64 * LRM_WAVES), 0, stream, kp, vp, k_new,
                        v_new, n_new, t0, batch, seq);

@@ -165,3 +165,27 @@ def test_lowrank_prefill_ragged_tail(gpu):
             xb = np.concatenate([np.zeros((1, Ts0[b], wl.Hkv, 128), np.float32), x[b:b + 1]], axis=1)
             rings.append(OL.tail_ring(xb, 64))
         assert np.array_equal(buf["tail"], OL.pack_tail(np.concatenate(rings))), name
+
+
+def test_lowrank_every_rank_and_width(gpu):
+    """Every (rank, bits) a low-rank head can take (ranks 16, 32, 64, 128 x
+    1-4 bits: rows of 2 to 64 bytes, tiled in 2- to 16-byte chunks), one kv
+    head each, through the matrix-core prefill path (runs of 280 and 19
+    tokens) and the one-token path: codes follow the tie rule against the
+    oracle and the decode over them matches the oracle's."""
+    table = tuple((r, b) for r in (16, 32, 64, 128) for b in (1, 2, 3, 4))
+    wl = synth.WORKLOADS["lowrank_1bpd"].with_(B=1, Hkv=16, Hq=32, T=300, N=0, lowrank=table)
+    k = synth.layer_rows(wl, 0, "k")
+    v = synth.layer_rows(wl, 0, "v")
+    gk, gv, ok_, ov = H.specs(wl)
+    cache = H.new_cache(wl, 320, gk, gv, gpu, N=0)
+    T = _append_chunks(cache, k, v, [280, 1, 19], gpu)
+    encs = {}
+    for name, x, spec in (("k", k.numpy(), ok_), ("v", v.numpy(), ov)):
+        encs[name], _ = H.unpack(cache, name, spec, T)
+        for h in range(wl.Hkv):
+            H.check_rotated_head(x[0, :, h, :], encs[name][0][h], spec, h)
+    q = synth.queries(wl, 0)
+    out = cache.decode(q.to(gpu), wl.sm_scale).cpu().numpy().astype(np.float64)
+    ref = OL.decode(q.numpy(), encs["k"], encs["v"], None, None, ok_, ov, T, 0, wl.sm_scale)
+    assert np.max(np.abs(out - ref)) <= H.ATOL
