@@ -423,6 +423,51 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // BF: the binary16 rows are bfloat16 (precision tail in bfloat16); only for
 // the all-16-bit configuration.
+// ------------------------------------------------ workgroup merge of waves --
+// After the tile loops every wave holds a softmax state (m, l, o) per head.
+// Each wave publishes its m, scales its own l and o by 2^(m_w - M) (M = the
+// maximum over the workgroup's waves) and the split's partial is then a
+// plain sum over the waves: one exponential per wave and head instead of one
+// per wave, head and channel.
+__device__ __forceinline__ float *merge_slots() {
+  __shared__ float s[NWAVE * 8];   // [wave][head] m
+  return s;
+}
+
+__device__ __forceinline__ float merge_max(const float *mw, int h) {
+  float M = NEG_INF;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mw[w * 8 + h]);
+  return M;
+}
+
+// Scale of wave state m for head h: 2^(m - M), zero for a wave without tokens.
+__device__ __forceinline__ float merge_scale(const float *mw, int h, float m) {
+  return m == NEG_INF ? 0.f : exp2f(m - merge_max(mw, h));
+}
+
+// mg: [wave][h][4 + NV] (l at 1, scaled o at 4..), already scaled.
+template <int HG, int NV>
+__device__ __forceinline__ void merge_store(const float *mg, const float *mw, float *part,
+                                            long long head_stride) {
+  constexpr int MS = NV + 4;
+  for (int idx = threadIdx.x; idx < HG * NV; idx += WG) {
+    const int h = idx / NV, c = idx % NV;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) o += mg[(w * HG + h) * MS + 4 + c];
+    float *dst = part + h * head_stride;
+    store_agent(dst + 4 + c, o);
+    if (c == 0) {
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWAVE; ++w) L += mg[(w * HG + h) * MS + 1];
+      store_agent(dst, merge_max(mw, h));
+      store_agent(dst + 1, L);
+    }
+  }
+}
+
 template <class C, bool BF = false>
 __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
   constexpr int HG = C::HG, TT = C::TT, NT = C::NT, NDT = C::NDT, NBV = C::NBV;
@@ -785,49 +830,33 @@ __device__ void attend_range(const SplitIO &io, uint8_t *lds) {
 #pragma unroll
     for (int j = 0; j < NBV; ++j) pmsum[j][k] = C::VFAM == FAM_1 ? row_sum16(pm[j][k]) : 0.f;
   }
-  __syncthreads();   // every wave is done with its LDS tiles
+  float *mw = merge_slots();
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (2 * g + k < HG && n == 0) mw[wave * 8 + 2 * g + k] = m_run[k];
+  __syncthreads();   // every wave is done with its LDS tiles; wave maxima published
 
-  // merge area: [wave][h][4 + NV]: m, l, -, -, o[NV]
+  // merge area: [wave][h][4 + NV]: -, l, -, -, o[NV], scaled to the
+  // workgroup maximum
   float *mg = reinterpret_cast<float *>(lds);
   constexpr int MS = C::NV + 4;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int h = 2 * g + k;
     if (h < HG) {
+      const float f = merge_scale(mw, h, m_run[k]);
       float *dst = mg + (wave * HG + h) * MS;
-      if (n == 0) {
-        dst[0] = m_run[k];
-        dst[1] = lsum[k];
-      }
+      if (n == 0) dst[1] = lsum[k] * f;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         float o = O[dt][k];
         if constexpr (C::VFAM == FAM_1) o += pmsum[(16 * dt) / C::LV][k];
-        dst[4 + 16 * dt + n] = o;
+        dst[4 + 16 * dt + n] = o * f;
       }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < HG * C::NV; idx += WG) {
-    const int h = idx / C::NV, c = idx % C::NV;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mg[(w * HG + h) * MS]);
-    float o = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-      const float *src = mg + (w * HG + h) * MS;
-      const float wt = src[0] == NEG_INF ? 0.f : exp2f(src[0] - M);
-      o = fmaf(wt, src[4 + c], o);
-      L = fmaf(wt, src[1], L);
-    }
-    float *dst = io.part + h * io.part_head_stride;
-    store_agent(dst + 4 + c, o);
-    if (c == 0) {
-      store_agent(dst, M);
-      store_agent(dst + 1, L);
-    }
-  }
+  merge_store<HG, C::NV>(mg, mw, io.part, io.part_head_stride);
 }
 
 #include "kvq_decode_q.hpp"
@@ -1010,6 +1039,9 @@ __device__ __forceinline__ void run_tail(const DecodeArgs &a, const Splits &sp, 
 // are in the stored basis and go back to the raw basis first (Hadamard
 // transform and 1/w for KVarN, P_h for low rank) before they meet the tail
 // partials.  `olow` holds 128 floats of LDS.
+// ONE: body and tail partials share the raw basis (plain layers), so all
+// splits merge into one accumulator.
+template <bool ONE>
 __device__ __forceinline__ void combine_head(const DecodeArgs &a, const Splits &sp, float *__restrict__ out,
                                              int b, int h, float *olow) {
   const int lane = threadIdx.x & 63;
@@ -1037,6 +1069,21 @@ __device__ __forceinline__ void combine_head(const DecodeArgs &a, const Splits &
       v[k] = load2_agent(po + (unsigned)(i * PSTRIDE));
     }
     const bool own = lane < cnt, body = sl < Sb;
+    if constexpr (ONE) {
+      const float nm = fmaxf(mb, wave_max(own ? ml.x : NEG_INF));
+      const float cb = mb == NEG_INF ? 0.f : exp2f(mb - nm);
+      lb *= cb; ob0 *= cb; ob1 *= cb;
+      mb = nm;
+      const float wgt = !own || ml.x == NEG_INF ? 0.f : exp2f(ml.x - mb);
+      lb += wave_sum(wgt * ml.y);
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float wk = read_lane(wgt, k);
+        ob0 = fmaf(wk, v[k].x, ob0);
+        ob1 = fmaf(wk, v[k].y, ob1);
+      }
+      continue;
+    }
     const float xb = wave_max(own && body ? ml.x : NEG_INF), xt = wave_max(own && !body ? ml.x : NEG_INF);
     // rescale what earlier batches summed to the new segment maxima
     const float nmb = fmaxf(mb, xb), nmt = fmaxf(mt, xt);
@@ -1066,7 +1113,7 @@ __device__ __forceinline__ void combine_head(const DecodeArgs &a, const Splits &
 
   // body sum back to the raw basis
   const int g = h / a.G;
-  if (Sb > 0) {
+  if (!ONE && Sb > 0) {
     if (a.v.basis == KVQ_BASIS_HADAMARD) {
       float x0 = ob0 + ob1, x1 = ob0 - ob1;
 #pragma unroll
@@ -1105,6 +1152,16 @@ __device__ __forceinline__ void combine_head(const DecodeArgs &a, const Splits &
   reinterpret_cast<float2 *>(out + bh * D)[lane] = o;
 }
 
+// Word of unit u's completion counter: units u mod 16 sit in different
+// 4 KB pages of the counter region (u / 16 is the word within the page).
+// Device-scope atomics on one cache line are performed one after another,
+// so counters packed side by side made every unit's splits queue behind
+// the others' (up to 2 us on short contexts).
+__device__ __forceinline__ unsigned *unit_counter(const DecodeArgs &a, int unit) {
+  return a.cnt + (unit & (DECODE_CNT_PAGES - 1)) * (DECODE_MAX_UNITS / DECODE_CNT_PAGES) +
+         unit / DECODE_CNT_PAGES;
+}
+
 // After a split's partials are stored: count the split as finished (one
 // device-scope counter per unit in the workspace); the workgroup that
 // finishes its unit last merges the unit's heads (wave w takes head w of
@@ -1114,15 +1171,18 @@ __device__ __forceinline__ void finish_split(const DecodeArgs &a, const Splits &
   __shared__ unsigned s_last;
   __builtin_amdgcn_s_waitcnt(0);           // this thread's partial stores completed
   __syncthreads();
-  unsigned *cnt = a.cnt + ((long long)b * a.Hkv + kvh) * a.NHG + hg;
+  unsigned *cnt = unit_counter(a, (b * a.Hkv + kvh) * a.NHG + hg);
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              (unsigned)(sp.sb + sp.st - 1);
   __syncthreads();
   if (!s_last) return;
   const int w = threadIdx.x >> 6;
-  if (w < a.HG)
-    combine_head(a, sp, a.out, b, kvh * a.G + hg * a.HG + w, reinterpret_cast<float *>(lds) + w * D);
+  if (w < a.HG) {
+    float *olow = reinterpret_cast<float *>(lds) + w * D;
+    if (a.v.basis == KVQ_BASIS_PLAIN) combine_head<true>(a, sp, a.out, b, kvh * a.G + hg * a.HG + w, olow);
+    else combine_head<false>(a, sp, a.out, b, kvh * a.G + hg * a.HG + w, olow);
+  }
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

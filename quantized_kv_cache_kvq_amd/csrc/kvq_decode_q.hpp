@@ -577,20 +577,23 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
 #pragma unroll
     for (int j = 0; j < NBV; ++j) pmsum[rg][j] = C::VFAM == FAM_1 ? row_sum16(pm[rg][j]) : 0.f;
   }
-  __syncthreads();   // every wave is done with its LDS tiles
+  float *mw = merge_slots();
+#pragma unroll
+  for (int rg = 0; rg < HGRP; ++rg)
+    if (g + 4 * rg < HG && n == 0) mw[wave * 8 + g + 4 * rg] = m_run[rg];
+  __syncthreads();   // every wave is done with its LDS tiles; wave maxima published
 
-  // merge area: [wave][h][4 + NV]: m, l, -, -, o[NV] (raw channel order)
+  // merge area: [wave][h][4 + NV]: -, l, -, -, o[NV] (raw channel order),
+  // scaled to the workgroup maximum
   float *mg = reinterpret_cast<float *>(lds);
   constexpr int MS = Q::NV + 4;
 #pragma unroll
   for (int rg = 0; rg < HGRP; ++rg) {
     const int h = g + 4 * rg;
     if (h < HG) {
+      const float f = merge_scale(mw, h, m_run[rg]);
       float *dst = mg + (wave * HG + h) * MS;
-      if (n == 0) {
-        dst[0] = m_run[rg];
-        dst[1] = lsum[rg];
-      }
+      if (n == 0) dst[1] = lsum[rg] * f;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int pos = 16 * dt + n;                       // staged byte position
@@ -598,32 +601,13 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
           const int ch = 8 * (pos >> 3) + grp8_perm<VB>(pos & 7);
           float o = O[rg][dt];
           if constexpr (C::VFAM == FAM_1) o += pmsum[rg][pos / Q::LV];
-          dst[4 + ch] = o;
+          dst[4 + ch] = o * f;
         }
       }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < HG * Q::NV; idx += WG) {
-    const int h = idx / Q::NV, c = idx % Q::NV;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, mg[(w * HG + h) * MS]);
-    float o = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-      const float *src = mg + (w * HG + h) * MS;
-      const float wt = src[0] == NEG_INF ? 0.f : exp2f(src[0] - M);
-      o = fmaf(wt, src[4 + c], o);
-      L = fmaf(wt, src[1], L);
-    }
-    float *dst = io.part + h * io.part_head_stride;
-    store_agent(dst + 4 + c, o);
-    if (c == 0) {
-      store_agent(dst, M);
-      store_agent(dst + 1, L);
-    }
-  }
+  merge_store<HG, Q::NV>(mg, mw, io.part, io.part_head_stride);
   // low rank: the channels past the rank are zero, so the combine (which
   // reads all 128 of every split) never meets stale workspace contents
   if constexpr (Q::NV < D) {

@@ -80,9 +80,12 @@ void timing_commit();
 // Split-K decode workgroups: waves per workgroup and workgroups resident
 // per CU (the split policy sizes one round of workgroups from these).
 constexpr int DECODE_WG_WAVES = 8;
-// Completion counters at the start of every decode workspace.
+// Completion counters at the start of every decode workspace, spread over
+// DECODE_CNT_PAGES pages of 4 KB.
 constexpr int DECODE_MAX_UNITS = 16384;
+constexpr int DECODE_CNT_PAGES = 16;
 constexpr size_t DECODE_CNT_BYTES = DECODE_MAX_UNITS * sizeof(unsigned);
+static_assert(DECODE_CNT_BYTES == DECODE_CNT_PAGES * 4096, "counter pages are 4 KB");
 constexpr int DECODE_WG_PER_CU = 1;
 
 int decode_tile_tokens(int kcodec, int vcodec, int basis);
