@@ -235,6 +235,18 @@ __device__ __forceinline__ half8 bytes_to_half8(uint2 x, float off) {
   return o.h;
 }
 
+// Byte codes u <= 15 -> exact binary16 u: an E4M3 byte below 16 encodes
+// u * 2^-9 (subnormal for u < 8, exponent 1 above), so the gfx950 scaled
+// fp8 conversion with scale 2^9 gives u itself, two bytes per instruction.
+__device__ __forceinline__ half8 small_bytes_to_half8(uint2 x) {
+  H8 o;
+  o.u[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 512.f, false));
+  o.u[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 512.f, true));
+  o.u[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 512.f, false));
+  o.u[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 512.f, true));
+  return o.h;
+}
+
 // ------------------------------------------------ QK operand preparation --
 
 // Raw codes of (k-block j, k-group kg) of one token: the 8 channels

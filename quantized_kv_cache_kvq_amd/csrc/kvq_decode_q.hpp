@@ -95,6 +95,13 @@ struct QCfg {
   // stored code = byte + KBIAS (the K operand bytes)
   static constexpr int KBIAS = C::KFAM == FAM_0 ? (KB == 8 ? 0 : -(1 << (KB - 1))) : (KB == 8 ? 128 : 0);
   static constexpr float VOFF = C::VFAM == FAM_0 ? (float)(1 << (VB - 1)) : 0.f;
+  // Value codes of at most 4 bits (u <= 15) reach the PV matrix cores as
+  // binary16 u through the fp8 (E4M3) conversion, exact for bytes below 16
+  // once scaled by 2^9; a _0 code's offset then moves to a per-block term
+  // -VOFF * sum_t p_t d_t, accumulated like the _1 minima.
+  static constexpr bool VCVT = VB <= 4;
+  static constexpr bool VMIN = C::VFAM == FAM_1 || (VCVT && C::VFAM == FAM_0);
+  static constexpr float VMINF = C::VFAM == FAM_1 ? 1.f : -VOFF;
   static constexpr int VPITCH = NV + 16;               // staged value row (bytes)
   static constexpr int W_V = TT * VPITCH;
   static constexpr int W_A = NBV * TT * 32;            // [j][t][16 rows] binary16
@@ -478,6 +485,10 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
         ps += p[rg][nt];
       }
       l_lane[rg] = fmaf(l_lane[rg], alpha[rg], ps);
+      if constexpr (C::VFAM != FAM_1 && Q::VMIN) {
+#pragma unroll
+        for (int j = 0; j < NBV; ++j) pm[rg][j] *= alpha[rg];
+      }
       if constexpr (C::VFAM == FAM_1) {
 #pragma unroll
         for (int j = 0; j < NBV; ++j) {
@@ -528,6 +539,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
           uint32_t *dst = reinterpret_cast<uint32_t *>(alds + ((j * TT) + 16 * nt + n) * 32 + 8 * g);
 #pragma unroll
           for (int rg = 0; rg < HGRP; ++rg) {
+            if constexpr (C::VFAM != FAM_1 && Q::VMIN) pm[rg][j] = fmaf(p[rg][nt], dv[j], pm[rg][j]);
             const float x = p[rg][nt] * scl;
             const _Float16 hi = (_Float16)x;
             const _Float16 lo = (_Float16)(x - (float)hi);
@@ -553,7 +565,9 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
         for (int d = 0; d < Q::DPB; ++d) {
           const int dt = j * Q::DPB + d;
           const uint8_t *pb = vlds + (tok + (n >> 1)) * Q::VPITCH + 16 * dt + 8 * (n & 1);
-          const half8 bv = bytes_to_half8(tr8(pb), Q::VOFF);
+          half8 bv;
+          if constexpr (Q::VCVT) bv = small_bytes_to_half8(tr8(pb));
+          else bv = bytes_to_half8(tr8(pb), Q::VOFF);
           ct[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, ct[dt], 0, 0, 0);
         }
       }
@@ -575,7 +589,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
   for (int rg = 0; rg < HGRP; ++rg) {
     lsum[rg] = row_sum16(l_lane[rg]);
 #pragma unroll
-    for (int j = 0; j < NBV; ++j) pmsum[rg][j] = C::VFAM == FAM_1 ? row_sum16(pm[rg][j]) : 0.f;
+    for (int j = 0; j < NBV; ++j) pmsum[rg][j] = Q::VMIN ? Q::VMINF * row_sum16(pm[rg][j]) : 0.f;
   }
   float *mw = merge_slots();
 #pragma unroll
@@ -600,7 +614,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
         if (pos < Q::NV) {
           const int ch = 8 * (pos >> 3) + grp8_perm<VB>(pos & 7);
           float o = O[rg][dt];
-          if constexpr (C::VFAM == FAM_1) o += pmsum[rg][pos / Q::LV];
+          if constexpr (Q::VMIN) o += pmsum[rg][pos / Q::LV];
           dst[4 + ch] = o * f;
         }
       }

@@ -269,6 +269,17 @@ def unit_bound(qg, kenc, venc, ktail, vtail, kspec, vspec, g, T, N, sm_scale, ta
                     m_raw = (p[body, None] * mv[body]).sum(0)
                 else:
                     m_raw = np.zeros(Yv.shape[1])
+                fam_v, bits_v = CODECS[vc]
+                if kc != "f16" and fam_v == "0" and bits_v <= 4:
+                    # integer path, codes of <= 4 bits: the PV sums u d (u the
+                    # offset-binary code) and the offset 2^(b-1) sum_t p_t d_t
+                    # is a separate binary32 term, like a _1 minimum; the
+                    # accumulator then holds magnitudes up to sum p (|v| + off)
+                    dv = np.abs(np.asarray(venc["scales"][:T], np.float64))
+                    off = np.repeat(dv, Lv, axis=1)[:, : Yv.shape[1]] * float(1 << (bits_v - 1))
+                    off_raw = (p[body, None] * off[body]).sum(0)
+                    m_raw = m_raw + off_raw
+                    floor = floor + 2.0 ** -20 * off_raw
                 ob = (p[body, None] * np.abs(Yv[body])).sum(0) + m_raw     # stored-basis magnitudes
                 if vspec.basis == "hadamard":
                     wv = vspec.w[g].astype(np.float64)
