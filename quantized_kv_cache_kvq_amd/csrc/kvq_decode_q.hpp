@@ -35,6 +35,17 @@ __host__ __device__ constexpr int grp8_perm(int e) {
        : e;
 }
 
+// Channel held by staged value byte `pos` of a row.  2-bit rows are staged
+// a 32-bit word (16 codes, code i at bits 2i) at a time: byte 4k + i of the
+// word's 16 bytes holds code 4i + k, so the four bytes of (w >> 2k) &
+// 0x03030303 go out as one word.  Other widths: 8-channel groups,
+// grp8_perm.
+template <int B>
+__host__ __device__ constexpr int vstage_ch(int pos) {
+  return B == 2 ? 16 * (pos >> 4) + 4 * (pos & 3) + ((pos >> 2) & 3)
+                : 8 * (pos >> 3) + grp8_perm<B>(pos & 7);
+}
+
 // Four B-bit codes (LSB first in the low 4*B bits of v; higher bits are
 // ignored) spread to the four bytes of a word, code i in byte i: codes 2, 3
 // move up to bit 16, then codes 1, 3 up by 8 - B.
@@ -396,8 +407,16 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
     const int lim = t_end - 1 - t0;
 
     // ---- value row of token `lane` into LDS as offset-binary bytes; byte
-    // 8G + e holds channel 8G + grp8_perm<VB>(e)
-    {
+    // pos holds channel vstage_ch<VB>(pos)
+    if constexpr (VB == 2) {
+      uint8_t *dst = vlds + lane * Q::VPITCH;
+#pragma unroll
+      for (int m = 0; m < Q::NV / 16; ++m) {
+        const uint32_t x = vw[m] ^ (C::VFAM == FAM_0 ? 0xAAAAAAAAu : 0u);
+        *reinterpret_cast<uint4 *>(dst + 16 * m) =
+            make_uint4(x & 0x03030303u, (x >> 2) & 0x03030303u, (x >> 4) & 0x03030303u, (x >> 6) & 0x03030303u);
+      }
+    } else {
       uint8_t *dst = vlds + lane * Q::VPITCH;
 #pragma unroll
       for (int G = 0; G < Q::NV / 8; ++G) {
@@ -612,7 +631,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
       for (int dt = 0; dt < NDT; ++dt) {
         const int pos = 16 * dt + n;                       // staged byte position
         if (pos < Q::NV) {
-          const int ch = 8 * (pos >> 3) + grp8_perm<VB>(pos & 7);
+          const int ch = vstage_ch<VB>(pos);
           float o = O[rg][dt];
           if constexpr (Q::VMIN) o += pmsum[rg][pos / Q::LV];
           dst[4 + ch] = o * f;
