@@ -149,6 +149,33 @@ def test_workspace_reuse_across_calls_and_shapes(gpu):
             torch.cuda.synchronize()
             err = np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref))
             assert err <= H.ATOL, (T, N, Hq, splits, step, err)
+            assert int(ws[: 1 << 16].count_nonzero()) == 0, (T, N, Hq, splits, step)
+
+
+def test_counters_left_zero_many_units(gpu):
+    """Each (batch entry, kv head, head group) has its own completion
+    counter (units u and u + 16 share a 4 KiB page at different words);
+    with more units than pages every counter must be back at zero after a
+    call and the outputs must match the oracle on repeated calls."""
+    wl = synth.WORKLOADS["gqa4_q8k_q4v_tail1024"].with_(B=3, T=900, N=128)
+    k = synth.layer_rows(wl, 0, "k").numpy()
+    v = synth.layer_rows(wl, 0, "v").numpy()
+    q = synth.queries(wl, 0)
+    gk, gv, ok_, ov = H.specs(wl)
+    cache = H.new_cache(wl, 960, gk, gv, gpu, N=128)
+    kenc, kp, kt = H.oracle_layer_bytes(k, ok_, 960, 128)
+    venc, vp, vt = H.oracle_layer_bytes(v, ov, 960, 128)
+    H.upload(cache, "k", kp, kt)
+    H.upload(cache, "v", vp, vt)
+    cache.n_tokens = wl.T
+    ref = OL.decode(q.numpy(), kenc, venc, OL.tail_ring(k, 128), OL.tail_ring(v, 128), ok_, ov,
+                    wl.T, 128, wl.sm_scale)
+    ws = cache.workspace(wl.Hq)
+    for splits in (0, 5, 0):
+        out = cache.decode(q.to(gpu), wl.sm_scale, body_splits=splits, ws=ws)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(out.cpu().numpy().astype(np.float64) - ref)) <= H.ATOL, splits
+        assert int(ws[: 1 << 16].count_nonzero()) == 0, splits
 
 
 @pytest.mark.parametrize("N", [0, 128])
