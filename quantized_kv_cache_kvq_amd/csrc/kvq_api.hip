@@ -183,10 +183,11 @@ constexpr double PLAN_TILE_COST = 16384.0;
 
 // Relative decode time of a low-rank head's body per tile, by bits (1..4)
 // and rank (16, 32, 64, 128): measured on MI355X as the kernel time of a
-// layer whose eight heads all share that (rank, bits), 8 sequences of 64k
-// tokens, less the fixed per-launch part.  Other pairs: rank-proportional.
+// layer whose eight heads all share that (rank, bits), 8 sequences of 128k
+// tokens, less the fixed per-launch part (~10 us).  Other pairs:
+// rank-proportional.
 double lowrank_tile_cost(int codec, int rank) {
-  static const double cost[4][4] = {{37, 36, 58, 113}, {38, 37, 60, 116}, {52, 51, 86, 172}, {36, 38, 64, 130}};
+  static const double cost[4][4] = {{74, 79, 121, 219}, {77, 78, 120, 227}, {106, 104, 169, 338}, {76, 81, 137, 263}};
   const int bits = codec_bits(codec);
   const int ri = rank == 16 ? 0 : rank == 32 ? 1 : rank == 64 ? 2 : rank == 128 ? 3 : -1;
   if (codec_family(codec) == FAM_1 && bits >= 1 && bits <= 4 && ri >= 0) return cost[bits - 1][ri];
