@@ -46,6 +46,22 @@ __host__ __device__ constexpr int vstage_ch(int pos) {
                 : 8 * (pos >> 3) + grp8_perm<B>(pos & 7);
 }
 
+// vstage_ch is a permutation of a 128-channel row for every width.
+template <int B>
+constexpr bool vstage_is_permutation() {
+  bool seen[128] = {};
+  for (int pos = 0; pos < 128; ++pos) {
+    const int ch = vstage_ch<B>(pos);
+    if (ch < 0 || ch >= 128 || seen[ch]) return false;
+    seen[ch] = true;
+  }
+  return true;
+}
+static_assert(vstage_is_permutation<1>() && vstage_is_permutation<2>() && vstage_is_permutation<3>() &&
+                  vstage_is_permutation<4>() && vstage_is_permutation<5>() && vstage_is_permutation<6>() &&
+                  vstage_is_permutation<8>(),
+              "staged value bytes map one to one onto channels");
+
 // Four B-bit codes (LSB first in the low 4*B bits of v; higher bits are
 // ignored) spread to the four bytes of a word, code i in byte i: codes 2, 3
 // move up to bit 16, then codes 1, 3 up by 8 - B.
