@@ -87,6 +87,41 @@ def test_codec_pairs(gpu, kc, vc):
     _run(gpu, wl, 650, 128, 768, kc=kc, vc=vc, splits=(0, 2))
 
 
+@pytest.mark.parametrize("kc,vc", [("q8_0", "q4_0"), ("q8_0", "q3_0"), ("q8_0", "q2_0"),
+                                   ("q8_1", "q4_1"), ("q1_1", "q1_1")])
+def test_cancelling_values_low_bit(gpu, kc, vc):
+    """Value codes of at most 4 bits reach the PV matrix cores unsigned,
+    with the _0 offset (or the _1 minimum) added as a separate per-block
+    term.  Values that alternate in sign token by token, at the codes'
+    extremes, under near-uniform weights make the output a small difference
+    of large sums: it must still match the oracle within the tolerance and
+    the derived bound."""
+    wl = synth.WORKLOADS["vbr_32layer"].with_(Hkv=2, Hq=8, T=700, N=64)
+    T, N, cap = 700, 64, 768
+    rng = np.random.default_rng(11)
+    k = (0.01 * rng.standard_normal((1, T, 2, 128))).astype(np.float32)
+    sign = np.where(np.arange(T) % 2 == 0, 1.0, -1.0)[None, :, None, None]
+    v = (sign * (1.0 + 0.001 * rng.standard_normal((1, T, 2, 128)))).astype(np.float32)
+    q = synth.queries(wl, 0)
+    gk, gv, ok_, ov = H.specs(wl, kcodec=kc, vcodec=vc)
+    cache = H.new_cache(wl, cap, gk, gv, gpu, N=N)
+    kenc, kp, kt = H.oracle_layer_bytes(k, ok_, cap, N)
+    venc, vp, vt = H.oracle_layer_bytes(v, ov, cap, N)
+    H.upload(cache, "k", kp, kt)
+    H.upload(cache, "v", vp, vt)
+    cache.n_tokens = T
+    ref = OL.decode(q.numpy(), kenc, venc, OL.tail_ring(k, N), OL.tail_ring(v, N), ok_, ov, T, N,
+                    wl.sm_scale)
+    bound = H.decode_bound(q.numpy(), kenc, venc, OL.tail_ring(k, N), OL.tail_ring(v, N), ok_, ov,
+                           T, N, wl.sm_scale)
+    for splits in (0, 3):
+        out = cache.decode(q.to(gpu), wl.sm_scale, body_splits=splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(got - ref)) <= H.ATOL, (vc, splits)
+        H.check_precision(got, ref, bound, "cancelling values %s splits=%d" % (vc, splits))
+
+
 @pytest.mark.parametrize("Hq", [2, 4, 6, 12, 16, 24])
 def test_group_sizes(gpu, Hq):
     wl = synth.WORKLOADS["vbr_32layer"].with_(Hkv=2, Hq=Hq)
