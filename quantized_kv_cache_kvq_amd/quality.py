@@ -51,6 +51,11 @@ def _exact(q, K, V, G, sm_scale):
     return logp, o
 
 
+def kl_nats(logp, logp_h):
+    """KL(p || p_hat) in nats over the last axis, from log-weights."""
+    return (logp.exp() * (logp - logp_h)).sum(-1)
+
+
 def measure(layer, q_all, K, V, sm_scale):
     """Metrics of one built layer over queries q_all [n, B, Hq, 128]."""
     G = q_all.shape[2] // K.shape[2]
@@ -61,7 +66,7 @@ def measure(layer, q_all, K, V, sm_scale):
         logp, o = _exact(q, K, V, G, sm_scale)
         logp_h, o_h = _exact(q, Kh, Vh, G, sm_scale)
         out = layer.decode(q, sm_scale).double()
-        kl = (logp.exp() * (logp - logp_h)).sum(-1)         # [B, Hq]
+        kl = kl_nats(logp, logp_h)                          # [B, Hq]
         err = (out - o).norm(dim=-1) / o.norm(dim=-1)
         kls.append(kl.flatten())
         errs.append(err.flatten())
