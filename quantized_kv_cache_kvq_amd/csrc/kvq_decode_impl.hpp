@@ -76,20 +76,25 @@ __device__ __forceinline__ uint32_t split16(float x) {
 
 // ------------------------------------------------------------ DPP helpers --
 
-// All-reduce over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
+// All-reduce over the 16 lanes of a DPP row (lanes 16r .. 16r+15).  Row
+// rotations read only lanes of the same row; bound_ctrl only replaces the
+// zero `old` operand, so the values are those of a plain rotation.  The max
+// is IEEE maximum (NaN-propagating): no operand canonicalisation, and the
+// same value as maxNum for the scores and exponents it sees (no NaN).
+#define KVQ_ROR(x, ctrl) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, true))
 __device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xF, 0xF, false)));
-  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xF, 0xF, false)));
+  x = __builtin_elementwise_maximum(x, KVQ_ROR(x, 0x128));
+  x = __builtin_elementwise_maximum(x, KVQ_ROR(x, 0x124));
+  x = __builtin_elementwise_maximum(x, KVQ_ROR(x, 0x122));
+  x = __builtin_elementwise_maximum(x, KVQ_ROR(x, 0x121));
   return x;
 }
 
 __device__ __forceinline__ float row_sum16(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xF, 0xF, true));
   return x;
 }
 

@@ -150,7 +150,7 @@ __device__ __forceinline__ uint32_t row_max_u16x2(uint32_t x) {
   x = __builtin_bit_cast(uint32_t,                                                              \
                          __builtin_elementwise_max(__builtin_bit_cast(us2, x),                  \
                                                    __builtin_bit_cast(us2, (uint32_t)__builtin_amdgcn_update_dpp( \
-                                                       0, (int)x, ctrl, 0xF, 0xF, false))));
+                                                       0, (int)x, ctrl, 0xF, 0xF, true))));
   KVQ_STEP(0x128) KVQ_STEP(0x124) KVQ_STEP(0x122) KVQ_STEP(0x121)
 #undef KVQ_STEP
   return x;
@@ -483,16 +483,27 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
         if constexpr (KB == 8 && C::KFAM == FAM_1) { bb.x ^= 0x80808080u; bb.y ^= 0x80808080u; }
         kb[j] = (long)((uint64_t)bb.x | ((uint64_t)bb.y << 32));
       }
+      // the N-tile's matrix ops read its codes before the next tile's loads
+      // reuse their registers (loads issued first would land in other
+      // registers, copied back at the end of every tile)
+      typedef int intx4 __attribute__((ext_vector_type(4)));
+      intx4 cq[HGRP][NKB];
+#pragma unroll
+      for (int rg = 0; rg < HGRP; ++rg)
+#pragma unroll
+        for (int j = 0; j < NKB; ++j)
+          cq[rg][j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(qA[rg][j], kb[j], intx4{0, 0, 0, 0}, 0, 0, 0);
       load_k_nt(tn, limn, nt);          // N-tile nt's registers are free again
       const bool valid = 16 * nt + n <= lim;
 #pragma unroll
       for (int rg = 0; rg < HGRP; ++rg) {
+        // (summing from zero keeps the masked select below a branch the
+        // compiler skips for absent heads; starting from the first block's
+        // product instead made the six-head decode 4% slower)
         float a1 = 0.f, a2 = 0.f;
 #pragma unroll
         for (int j = 0; j < NKB; ++j) {
-          typedef int intx4 __attribute__((ext_vector_type(4)));
-          const intx4 z = {0, 0, 0, 0};
-          const intx4 c = __builtin_amdgcn_mfma_i32_16x16x32_i8(qA[rg][j], kb[j], z, 0, 0, 0);
+          const intx4 c = cq[rg][j];
           float f = fmaf((float)c[0], 16384.f, (float)(c[1] * 128 + c[2]));
           if constexpr (Q::KBIAS != 0) f += Qb[rg][j];
           a1 = fmaf(dk[j], f, a1);
@@ -510,7 +521,7 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
 #pragma unroll
       for (int nt = 1; nt < NT; ++nt) mx = fmaxf(mx, sc[rg][nt]);
       mx = row_max16(mx);
-      const float mnew = fmaxf(m_run[rg], mx);
+      const float mnew = __builtin_elementwise_maximum(m_run[rg], mx);   // no NaN: IEEE maximum, no canonicalisation
       alpha[rg] = m_run[rg] == NEG_INF ? (mnew == NEG_INF ? 1.f : 0.f) : __builtin_amdgcn_exp2f(m_run[rg] - mnew);
       m_run[rg] = mnew;
       float ps = 0.f;
@@ -576,9 +587,11 @@ __device__ void attend_q(const SplitIO &io, uint8_t *lds) {
           for (int rg = 0; rg < HGRP; ++rg) {
             if constexpr (C::VFAM != FAM_1 && Q::VMIN) pm[rg][j] = fmaf(p[rg][nt], dv[j], pm[rg][j]);
             const float x = p[rg][nt] * scl;
-            const _Float16 hi = (_Float16)x;
-            const _Float16 lo = (_Float16)(x - (float)hi);
-            dst[rg] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            h2 hl;
+            hl.x = (_Float16)x;                                   // hi
+            hl.y = (_Float16)(x - (float)hl.x);                   // lo, into the upper half
+            dst[rg] = __builtin_bit_cast(uint32_t, hl);
           }
         }
       }
