@@ -8,8 +8,8 @@ Inputs are device-generated; the oracle then checks, after the step:
 * 32k GQA workload: every K/V code, scale and tail byte of all 8 kv heads
   bit-exact against the oracle's encoding of the same inputs, and all 32
   query heads' outputs against the oracle's decode of that cache;
-* the other workloads (too large to re-encode whole on the host): sampled
-  (batch, kv head) units, each checked over its whole context: stored codes
+* the other workloads (too large to re-encode whole on the host at once):
+  every (batch, kv head) unit, one at a time over its whole context: stored codes
   under the tie rule of tests/helpers.py, and the unit's query heads'
   outputs against the oracle's attention over the unit's device cache;
 * the VBR workload: one layer per codec of the schedule at full context,
@@ -150,19 +150,23 @@ def test_gqa4_32k_all_heads(gpu):
     _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated=False)
 
 
-def test_kvarn_q3_64k_sampled(gpu):
+@pytest.mark.parametrize("entries", [(0, 1), (2, 3)])
+def test_kvarn_q3_64k_all_units(gpu, entries):
+    # every kv head of these batch entries (two tests, each well inside the
+    # per-test limit)
     wl = synth.WORKLOADS["kvarn_q3_tail2048"]
     cache, k, v, ok_, ov, out, qh = _build(gpu, wl)
-    units = [(0, h) for h in range(wl.Hkv)] + [(1, 5), (3, 7)]
+    units = [(b, h) for b in entries for h in range(wl.Hkv)]
     _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated=True)
 
 
-def test_lowrank_128k_sampled(gpu):
+@pytest.mark.parametrize("entries", [(0, 1, 2, 3), (4, 5, 6, 7)])
+def test_lowrank_128k_all_units(gpu, entries):
+    # every kv head (every rank and bit width of the table) of these batch
+    # entries; two tests so that each stays well inside the per-test limit
     wl = synth.WORKLOADS["lowrank_1bpd"]
     cache, k, v, ok_, ov, out, qh = _build(gpu, wl)
-    # every kv head (every rank and bit width of the table) of batch entry 0,
-    # and heads 3 and 6 of later entries
-    units = [(0, h) for h in range(wl.Hkv)] + [(5, 3), (7, 6)]
+    units = [(b, h) for b in entries for h in range(wl.Hkv)]
     _check_units(wl, cache, k, v, ok_, ov, out, qh, units, rotated=True)
 
 
