@@ -59,6 +59,11 @@ extern "C" {
 #define KVQ_HEAD_DIM 128        /* the only supported head_dim */
 #define KVQ_TILE_TOKENS 64      /* capacity and tail_len are multiples of this */
 #define KVQ_MAX_LOWRANK_HEADS 32
+/* Largest capacity and tail_len (tokens per plane).  Kernels address a
+ * token inside one (batch, kv head) plane with 32-bit offsets: 2^24 rows of
+ * at most 256 bytes (a binary16 row) stay below 2^32.  Larger layers are
+ * rejected with KVQ_ERR_INVALID_ARG before anything is enqueued. */
+#define KVQ_MAX_CAPACITY (1 << 24)
 
 typedef enum kvq_status {
     KVQ_OK = 0,
@@ -132,8 +137,8 @@ typedef struct kvq_layer {
     int32_t batch;              /* B >= 1 */
     int32_t n_kv_heads;         /* Hkv >= 1 (<= 32 for LOWRANK) */
     int32_t head_dim;           /* must be 128 */
-    int32_t capacity;           /* rows per plane, multiple of 64 */
-    int32_t tail_len;           /* N, multiple of 64, 0 = no tail */
+    int32_t capacity;           /* rows per plane, multiple of 64, <= KVQ_MAX_CAPACITY */
+    int32_t tail_len;           /* N, multiple of 64, 0 = no tail, <= KVQ_MAX_CAPACITY */
     int32_t n_tokens;           /* T tokens already cached, 0 <= T <= capacity */
     int32_t tail_format;        /* kvq_tail_format of both tails */
     const int32_t *seq_tokens;  /* NULL, or device [batch]: tokens of each

@@ -82,6 +82,9 @@ kvq_status check_layer(const kvq_layer *L) {
   if (L->tail_len < 0 || L->tail_len % KVQ_TILE_TOKENS)
     return fail(KVQ_ERR_INVALID_ARG, "tail_len %d must be a non-negative multiple of %d",
                 L->tail_len, KVQ_TILE_TOKENS);
+  if (L->capacity > KVQ_MAX_CAPACITY || L->tail_len > KVQ_MAX_CAPACITY)
+    return fail(KVQ_ERR_INVALID_ARG, "capacity %d / tail_len %d above KVQ_MAX_CAPACITY %d (32-bit in-plane offsets)",
+                L->capacity, L->tail_len, KVQ_MAX_CAPACITY);
   if (L->tail_format != KVQ_TAIL_F16 && L->tail_format != KVQ_TAIL_BF16)
     return fail(KVQ_ERR_INVALID_ARG, "tail_format %d is not a kvq_tail_format", L->tail_format);
   if (L->n_tokens < 0 || L->n_tokens > L->capacity)

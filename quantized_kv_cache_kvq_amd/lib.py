@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "kvq.h")
 
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(6)
+KVQ_MAX_CAPACITY = 1 << 24     # include/kvq.h: largest capacity / tail_len per plane
 
 CODECS = ["f16", "q8_0", "q6_0", "q5_0", "q4_0", "q3_0", "q2_0",
           "q8_1", "q6_1", "q5_1", "q4_1", "q3_1", "q2_1", "q1_1"]

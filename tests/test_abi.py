@@ -3,6 +3,7 @@ point, reports closed-form buffer sizes, and rejects bad arguments on the
 host before anything is launched (no compute call needs a GPU here)."""
 
 import ctypes
+import os
 
 import pytest
 
@@ -102,6 +103,26 @@ def test_host_validation_rejects_before_launch(L):
     d = _layer(T=64)
     assert L.kvq_dequantize(ctypes.byref(d), 2, 1, null) == lib.KVQ_ERR_INVALID_ARG
     assert L.kvq_dequantize(ctypes.byref(d), 0, null, null) == lib.KVQ_ERR_INVALID_ARG
+
+
+def test_capacity_above_maximum_rejected(L):
+    """Layers beyond KVQ_MAX_CAPACITY (32-bit in-plane offsets) are refused
+    by every compute entry point before anything is enqueued."""
+    import re
+    hdr = open(os.path.join(os.path.dirname(lib.HERE), "include", "kvq.h")).read()
+    m = re.search(r"#define KVQ_MAX_CAPACITY \(1 << (\d+)\)", hdr)
+    assert m and lib.KVQ_MAX_CAPACITY == 1 << int(m.group(1))
+    null = ctypes.c_void_p(0)
+    big = lib.KVQ_MAX_CAPACITY + 64
+    for d in (_layer(cap=big, T=10), _layer(cap=1024, N=big, T=10)):
+        assert L.kvq_quantize_append(ctypes.byref(d), 1, 1, 1, null) == lib.KVQ_ERR_INVALID_ARG
+        assert b"KVQ_MAX_CAPACITY" in L.kvq_last_error()
+        assert L.kvq_dequantize(ctypes.byref(d), 0, 1, null) == lib.KVQ_ERR_INVALID_ARG
+        assert L.kvq_transcode_layer(ctypes.byref(d), ctypes.byref(d), null) == lib.KVQ_ERR_INVALID_ARG
+        ws = (1, 32, ctypes.c_float(1.0), 1, 1, ctypes.c_size_t(1 << 30), null)
+        assert L.kvq_decode_attention(ctypes.byref(d), *ws) == lib.KVQ_ERR_INVALID_ARG
+        assert L.kvq_append_decode(ctypes.byref(d), 1, 1, 1, 32, ctypes.c_float(1.0), 1, 1,
+                                   ctypes.c_size_t(1 << 30), null) == lib.KVQ_ERR_INVALID_ARG
 
 
 def test_decode_validation(L):
